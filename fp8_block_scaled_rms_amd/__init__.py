@@ -1,0 +1,262 @@
+"""fp8q: the FP8 quantized linear layer of LLM inference on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in include/fp8q.h.  The binding
+only marshals arguments: every step of the computation runs in the HIP
+kernels of libfp8q.so.  PyTorch provides device memory and the current
+stream; there is no fallback of any kind, and every call raises if the
+library is missing or returns a non-OK status.
+
+Functions named fp8q_* mirror the C entry points one to one (outputs first,
+tensors in, sizes taken from the tensors).  The lower-case helpers
+(rmsnorm_quant, silu_mul_quant, quant, scaled_mm, scaled_mm_blockwise)
+allocate the outputs and the workspace with torch and call them.
+
+Data types: bf16 tensors are torch.bfloat16; e4m3 tensors are torch.uint8
+(raw OCP e4m3 bytes; ``t.view(torch.float8_e4m3fn)`` reinterprets them);
+scales are torch.float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PER_TOKEN = 0
+GROUP128 = 1
+OP_SCALED_MM = 0
+OP_SCALED_MM_BLOCKWISE = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+_STATUS = {
+    0: "FP8Q_OK", 1: "FP8Q_ERR_INVALID_ARG", 2: "FP8Q_ERR_UNSUPPORTED_SHAPE",
+    3: "FP8Q_ERR_ALIGNMENT", 4: "FP8Q_ERR_WORKSPACE", 5: "FP8Q_ERR_NO_DEVICE",
+    6: "FP8Q_ERR_ARCH", 7: "FP8Q_ERR_HIP", 8: "FP8Q_ERR_BAD_MODE", 9: "FP8Q_ERR_BAD_CONFIG",
+}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); the C declarations are in include/fp8q.h
+SIGNATURES = {
+    "fp8q_rmsnorm_quant": (_INT, [_P, _P, _P, _P, _I64, _I64, _F32, _INT, _P]),
+    "fp8q_silu_mul_quant": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
+    "fp8q_quant": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
+    "fp8q_scaled_mm": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "fp8q_scaled_mm_blockwise": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "fp8q_workspace_size": (_SZ, [_INT, _I64, _I64, _I64]),
+    "fp8q_gemm_num_configs": (_INT, []),
+    "fp8q_gemm_config_name": (ctypes.c_char_p, [_INT]),
+    "fp8q_gemm_config_for": (_INT, [_INT, _I64, _I64, _I64]),
+    "fp8q_workspace_size_cfg": (_SZ, [_INT, _I64, _I64, _I64]),
+    "fp8q_scaled_mm_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT, _P]),
+    "fp8q_scaled_mm_blockwise_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ,
+                                            _INT, _P]),
+    "fp8q_cvt_e4m3": (_INT, [_P, _P, _I64, _P]),
+    "fp8q_silu": (_INT, [_P, _P, _I64, _P]),
+    "fp8q_status_string": (ctypes.c_char_p, [_INT]),
+    "fp8q_last_hip_error": (_INT, []),
+    "fp8q_version": (_INT, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfp8q.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m fp8_block_scaled_rms_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().fp8q_status_string(status).decode()
+        if status == 7:
+            msg += f" (hipError {lib().fp8q_last_hip_error()})"
+        super().__init__(f"{where}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise Fp8qError(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t: torch.Tensor, dtypes, what: str):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+
+
+_E4M3 = (torch.uint8, torch.float8_e4m3fn)
+_BF16 = (torch.bfloat16,)
+_F32T = (torch.float32,)
+
+
+# ------------------------------------------------------------- C mirrors --
+
+def fp8q_rmsnorm_quant(q, scale, x, w, eps: float, mode: int, stream=None) -> None:
+    _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x"); _need(w, _BF16, "w")
+    M, K = x.shape
+    _check(lib().fp8q_rmsnorm_quant(_ptr(q), _ptr(scale), _ptr(x), _ptr(w), M, K, eps, mode,
+                                    _stream(stream)), "fp8q_rmsnorm_quant")
+
+
+def fp8q_silu_mul_quant(q, scale, gate_up, mode: int, stream=None) -> None:
+    _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(gate_up, _BF16, "gate_up")
+    M, twoD = gate_up.shape
+    _check(lib().fp8q_silu_mul_quant(_ptr(q), _ptr(scale), _ptr(gate_up), M, twoD // 2, mode,
+                                     _stream(stream)), "fp8q_silu_mul_quant")
+
+
+def fp8q_quant(q, scale, x, mode: int, stream=None) -> None:
+    _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x")
+    M, K = x.shape
+    _check(lib().fp8q_quant(_ptr(q), _ptr(scale), _ptr(x), M, K, mode, _stream(stream)),
+           "fp8q_quant")
+
+
+def fp8q_scaled_mm(y, a, b, sa, sb, ws=None, cfg: int | None = None, stream=None) -> None:
+    _need(y, _BF16, "y"); _need(a, _E4M3, "a"); _need(b, _E4M3, "b")
+    _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    if cfg is None:
+        rc = lib().fp8q_scaled_mm(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K,
+                                  _ptr(ws), wsb, _stream(stream))
+    else:
+        rc = lib().fp8q_scaled_mm_cfg(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K,
+                                      _ptr(ws), wsb, cfg, _stream(stream))
+    _check(rc, "fp8q_scaled_mm")
+
+
+def fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws=None, cfg: int | None = None,
+                             stream=None) -> None:
+    _need(y, _BF16, "y"); _need(a, _E4M3, "a"); _need(b, _E4M3, "b")
+    _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    if cfg is None:
+        rc = lib().fp8q_scaled_mm_blockwise(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N,
+                                            K, _ptr(ws), wsb, _stream(stream))
+    else:
+        rc = lib().fp8q_scaled_mm_blockwise_cfg(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M,
+                                                N, K, _ptr(ws), wsb, cfg, _stream(stream))
+    _check(rc, "fp8q_scaled_mm_blockwise")
+
+
+def fp8q_workspace_size(op: int, M: int, N: int, K: int, cfg: int | None = None) -> int:
+    if cfg is None:
+        return lib().fp8q_workspace_size(op, M, N, K)
+    return lib().fp8q_workspace_size_cfg(cfg, M, N, K)
+
+
+def fp8q_gemm_num_configs() -> int:
+    return lib().fp8q_gemm_num_configs()
+
+
+def fp8q_gemm_config_name(cfg: int) -> str:
+    n = lib().fp8q_gemm_config_name(cfg)
+    return n.decode() if n else None
+
+
+def fp8q_gemm_config_for(op: int, M: int, N: int, K: int) -> int:
+    return lib().fp8q_gemm_config_for(op, M, N, K)
+
+
+def fp8q_cvt_e4m3(q, x, stream=None) -> None:
+    _need(q, _E4M3, "q"); _need(x, _F32T, "x")
+    _check(lib().fp8q_cvt_e4m3(_ptr(q), _ptr(x), x.numel(), _stream(stream)), "fp8q_cvt_e4m3")
+
+
+def fp8q_silu(y, g, stream=None) -> None:
+    _need(y, _F32T, "y"); _need(g, _BF16, "g")
+    _check(lib().fp8q_silu(_ptr(y), _ptr(g), g.numel(), _stream(stream)), "fp8q_silu")
+
+
+def fp8q_version() -> int:
+    return lib().fp8q_version()
+
+
+# --------------------------------------------------- allocating helpers --
+
+def _scale_shape(M: int, K: int, mode: int):
+    return (M,) if mode == PER_TOKEN else (M, K // 128)
+
+
+def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, mode: int, stream=None):
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+    fp8q_rmsnorm_quant(q, s, x, w, eps, mode, stream)
+    return q, s
+
+
+def silu_mul_quant(gate_up: torch.Tensor, mode: int, stream=None):
+    M, twoD = gate_up.shape
+    D = twoD // 2
+    q = torch.empty((M, D), dtype=torch.uint8, device=gate_up.device)
+    s = torch.empty(_scale_shape(M, D, mode), dtype=torch.float32, device=gate_up.device)
+    fp8q_silu_mul_quant(q, s, gate_up, mode, stream)
+    return q, s
+
+
+def quant(x: torch.Tensor, mode: int, stream=None):
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+    fp8q_quant(q, s, x, mode, stream)
+    return q, s
+
+
+def _workspace(op, M, N, K, device, cfg=None):
+    nbytes = fp8q_workspace_size(op, M, N, K, cfg)
+    if nbytes == 0:
+        return None
+    return torch.empty(((nbytes + 3) // 4,), dtype=torch.float32, device=device)
+
+
+def scaled_mm(a, b, sa, sb, cfg: int | None = None, stream=None):
+    M, N = a.shape[0], b.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    ws = _workspace(OP_SCALED_MM, M, N, a.shape[1], a.device, cfg)
+    fp8q_scaled_mm(y, a, b, sa, sb, ws, cfg, stream)
+    return y
+
+
+def scaled_mm_blockwise(a, sa, b, sb, cfg: int | None = None, stream=None):
+    M, N = a.shape[0], b.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    ws = _workspace(OP_SCALED_MM_BLOCKWISE, M, N, a.shape[1], a.device, cfg)
+    fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws, cfg, stream)
+    return y

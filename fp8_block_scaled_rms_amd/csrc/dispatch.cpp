@@ -1,0 +1,79 @@
+// Per-shape choice of GEMM variant.
+//
+// The page "Helion can accelerate vLLM LLM inference on NVIDIA GPUs"
+// (aihirek.info), section "Autotuning picks the right variant", contrasts
+// hand-written dispatch rules with treating the algorithm (conventional,
+// split-K, swap-AB) as a tuned parameter chosen per input shape.  Here the
+// choice is a compiled-in table keyed by (op, N, K, M bucket) whose rows are
+// written from on-device measurements (tune_table.inc); shapes it does not
+// cover fall back to a fixed rule.  The lookup is a short linear scan of
+// static data: no allocation, no locks, no HIP calls.
+#include <cstring>
+
+#include "dispatch.h"
+#include "gemm_kernels.h"
+
+namespace fp8q {
+namespace {
+
+struct TableRow {
+  int op;
+  long n, k, m_max;
+  const char* variant;
+};
+
+const TableRow kTable[] = {
+#include "tune_table.inc"
+    {-1, 0, 0, 0, nullptr}};
+
+int find_variant(const char* name) {
+  const int n = gemm_num_configs();
+  for (int i = 0; i < n; ++i)
+    if (std::strcmp(gemm_config(i).name, name) == 0) return i;
+  return -1;
+}
+
+int find_skinny(int tm, int rw, int wk, int split) {
+  const int n = gemm_num_configs();
+  for (int i = 0; i < n; ++i) {
+    const GemmConfig& c = gemm_config(i);
+    if (c.kind == kSkinny && c.engine == kEngineExact && c.tm == tm && c.rw == rw &&
+        c.wk == wk && c.split == split)
+      return i;
+  }
+  return -1;
+}
+
+// Fixed rule for shapes without a measured row (exact engine only).
+int rule(int op, long M, long N, long K) {
+  (void)op;
+  if (M <= 128) {
+    const int tm = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    const int rw = (N % 32 == 0) ? 2 : 1;
+    const int wk = tm == 8 ? 4 : 8;
+    const long kb = K / 128;
+    int split = 1;
+    // enough workgroups to cover the chip twice, while every wave keeps
+    // at least two K blocks
+    while ((N / (16 * rw)) * split < 512 && split < 8 && kb / (2L * split) >= 2L * wk) split *= 2;
+    int id = find_skinny(tm, rw, wk, split);
+    if (id >= 0) return id;
+  }
+  if (N % 128 == 0) return find_variant("f16_tiled_m128_n128_w2x2");
+  return -1;
+}
+
+}  // namespace
+
+int dispatch_gemm(int op, long M, long N, long K) {
+  for (const TableRow* r = kTable; r->variant != nullptr; ++r) {
+    if (r->op == op && r->n == N && r->k == K && M <= r->m_max) {
+      const int id = find_variant(r->variant);
+      if (id >= 0 && gemm_config_fits(id, M, N, K)) return id;
+      break;
+    }
+  }
+  return rule(op, M, N, K);
+}
+
+}  // namespace fp8q

@@ -1,0 +1,48 @@
+// Internal launch interface of the FP8 GEMM kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+// One compiled GEMM variant.
+//   kind kTiled:  LDS-staged, double-buffered tiles of bn weight rows x bm
+//                 tokens, wn x wm waves; every operand byte is read from HBM
+//                 once per tile row/column.
+//   kind kSkinny: weight-streaming kernel for small M: a workgroup owns
+//                 rw*16 weight rows and all (<= tm*16) tokens, its wk waves
+//                 split K and are reduced through LDS; `split` > 1 also splits
+//                 K across workgroups through an fp32 workspace.
+// Both keep the weight rows on the 16-row side of the 16x16x128 MFMA and the
+// tokens on the 16-column side (the swap-AB orientation).
+enum GemmKind { kTiled = 0, kSkinny = 1 };
+
+// Accumulation engine (see gemm_kernels.hip): 0 = FP8 MFMA (fast, hardware
+// group-truncated sums), 1 = exact f16 MFMA on losslessly widened operands.
+enum GemmEngine { kEngineFp8 = 0, kEngineExact = 1 };
+
+struct GemmConfig {
+  const char* name;
+  int kind;
+  int engine;
+  int bm, bn, wm, wn;  // kTiled
+  int tm, rw, wk;      // kSkinny
+  int split;           // kSkinny: workgroups along K (1 = none)
+};
+
+int gemm_num_configs();
+const GemmConfig& gemm_config(int id);
+// Whether config `id` can run a problem of M tokens (the skinny kernel has a
+// compile-time token limit).
+bool gemm_config_fits(int id, long M, long N, long K);
+size_t gemm_workspace_bytes(int id, long M, long N, long K);
+
+// blockwise == false: per-token x per-channel scales (sa [M], sb [N]);
+// blockwise == true : sa [M, K/128], sb [N/128, K/128].
+hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, const float* sa,
+                       const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
+                       hipStream_t st);
+
+}  // namespace fp8q

@@ -1,0 +1,602 @@
+// FP8 (OCP e4m3) GEMMs with fp32 accumulation and bf16 output for gfx950.
+//
+//   scaled_mm            y[m,n] = sa[m] sb[n] sum_k a[m,k] b[n,k]
+//   scaled_mm_blockwise  y[m,n] = sum_kb sa[m,kb] sb[n/128,kb] sum_{k in kb} a[m,k] b[n,k]
+//
+// (page "Helion in vLLM: FP8 inference of Qwen3", 24-ai.news, section
+// "Kernels integrated into vLLM": scaled_mm and scaled_mm_blockwise).  Both
+// operands are K-contiguous ("NT": a [M,K] activations, b [N,K] weights).
+//
+// The matrix core step is v_mfma_scale_f32_16x16x128_f8f6f4 with neutral
+// E8M0 scales (2^0): one instruction consumes exactly one 128-wide K block,
+// so the blockwise scales are applied per instruction result in VALU
+// (acc += p * sa * sb) and never need a second accumulator.  Weight rows sit
+// on the MFMA's 16-row side and tokens on its 16-column side, so each lane's
+// four results share one token (one activation scale) and are four adjacent
+// output columns (one 8-byte bf16 store).  This is the swap-AB orientation
+// of the page "Helion can accelerate vLLM LLM inference on NVIDIA GPUs"
+// (aihirek.info), section "One GEMM implementation handles several
+// algorithms"; with a 16x16 instruction it costs nothing at large M.
+//
+// Operand fragments: lane l of a 16x128 fragment holds row (l % 16), bytes
+// [32 (l / 16), 32 (l / 16) + 32) of the 128-byte K block.  Both operands use
+// the same byte-to-K assignment, so the dot product is the same whatever
+// K order the hardware applies inside the instruction.  The result lane l
+// holds rows 4 (l / 16) + r, r = 0..3, of column l % 16.
+//
+// Two kernels:
+//  * tiled: for large M.  A workgroup stages a BN x 128 weight tile and a
+//    BM x 128 token tile per K block into LDS with direct global->LDS 16-byte
+//    loads (no VGPR round trip), double buffered, XOR-swizzled by 16-byte
+//    chunk so the fragment reads do not collide in LDS banks.
+//  * skinny: for small M (decode).  HBM traffic is the weight matrix; a
+//    workgroup streams rw*16 weight rows straight into registers, its wk
+//    waves take interleaved K blocks (split-K inside the workgroup) and are
+//    summed through LDS in a fixed order.  `split` > 1 additionally splits K
+//    across workgroups through an fp32 workspace and an ordered reduction
+//    (page above: split K when M or N is too small to fill the GPU).
+#include "fp8q_common.hpp"
+#include "gemm_kernels.h"
+
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace fp8q {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+constexpr int kBK = 128;  // K per stage = one scale block = one MFMA
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Accumulation engines for one 16x16 output tile over one 128-wide K block.
+//
+// kEngineF8: one v_mfma_scale_f32_16x16x128_f8f6f4 (operand formats e4m3,
+//   neutral E8M0 scales 2^0).  Fastest, but the FP8 datapath adds its 128
+//   products in groups of 8 aligned to the largest product of each group and
+//   drops the bits more than about 2^12 below it, so elements whose sum
+//   cancels heavily carry a relative error well above fp32 rounding.
+// kEngineF16: every e4m3 byte is widened exactly to f16 (each e4m3 value is
+//   representable in f16) with v_cvt_scalef32_pk_f16_fp8 and the block is
+//   four v_mfma_f32_16x16x32_f16, whose sums are exact to fp32 rounding.  Half
+//   the matrix-core rate of kEngineF8; the default wherever the table does not
+//   choose otherwise.
+// Both engines use the same 32-byte-per-lane fragments; kEngineF16 feeds
+// instruction s with bytes [8s, 8s+8) of each lane's 32, identically for both
+// operands, which is a fixed permutation of K inside the block.
+constexpr int kEngineF8 = kEngineFp8;
+constexpr int kEngineF16 = kEngineExact;
+
+__device__ __forceinline__ v8h widen8(int lo, int hi) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// A fragment prepared for an engine: the raw bytes (kEngineF8) or four f16
+// slabs (kEngineF16).
+template <int E>
+struct Frag;
+template <>
+struct Frag<kEngineF8> {
+  v8i b;
+};
+template <>
+struct Frag<kEngineF16> {
+  v8h h[4];
+};
+
+template <int E>
+__device__ __forceinline__ Frag<E> prep(const v8i& raw) {
+  Frag<E> f;
+  if constexpr (E == kEngineF8) {
+    f.b = raw;
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.h[s] = widen8(raw[2 * s], raw[2 * s + 1]);
+  }
+  return f;
+}
+
+// c + W_block * X_block^T for one tile (weights on the 16-row side).
+template <int E>
+__device__ __forceinline__ v4f block_mma(const Frag<E>& w, const Frag<E>& x, v4f c) {
+  if constexpr (E == kEngineF8) {
+    // operand formats 0 = e4m3; scale 127 = E8M0 2^0 on both sides
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.b, x.b, c, 0, 0, 0, 127, 0, 127);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.h[s], x.h[s], c, 0, 0, 0);
+    return c;
+  }
+}
+
+// Direct global -> LDS loads.  `lds` must be wave-uniform: lane i's data
+// lands at lds + i * size.
+__device__ __forceinline__ void g2lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds, 4, 0, 0);
+}
+
+// 16-byte-chunk swizzle of a 128-byte LDS row: rows 0..7 use distinct chunks
+// and rows of equal parity within 16 also do, so a 16-lane fragment read is
+// free of bank conflicts for 32 or 64 banks.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ v8i load_frag_lds(const uint8_t* tile, int r, int g) {
+  const uint8_t* row = tile + r * kBK;
+  const uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ swz(r)) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ swz(r)) << 4));
+  v8i f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+__device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  v8i f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* y, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = pack_bf16x2(a, b);
+  v.y = pack_bf16x2(c, d);
+  *reinterpret_cast<uint2*>(y) = v;
+}
+
+// ------------------------------------------------------------- tiled --
+template <int BM, int BN, int WM, int WN, bool BLOCK>
+struct TiledShape {
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int kTM = BM / WM;   // tokens per wave
+  static constexpr int kTN = BN / WN;   // weight rows per wave
+  static constexpr int kFT = kTM / 16;  // token fragments per wave
+  static constexpr int kFW = kTN / 16;  // weight fragments per wave
+  static constexpr int kXBytes = BM * kBK;
+  static constexpr int kWBytes = BN * kBK;
+  static constexpr int kStage = kXBytes + kWBytes + (BLOCK ? BM * 4 : 0);
+  static constexpr int kLds = 2 * kStage;
+  static_assert((BM * 8) % kThreads == 0 && (BN * 8) % kThreads == 0, "tile/threads");
+  static_assert(128 % kTN == 0, "a wave's weight rows must sit in one 128-row block");
+  static_assert(BM % 64 == 0, "token tile in whole waves for the scale load");
+};
+
+template <int BM, int BN, int WM, int WN, bool BLOCK, int E>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
+    uint16_t* __restrict__ y, const uint8_t* __restrict__ A, const float* __restrict__ sa,
+    const uint8_t* __restrict__ B, const float* __restrict__ sb, int M, int N, int K) {
+  using S = TiledShape<BM, BN, WM, WN, BLOCK>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN, wm = wave / WN;
+  const int lr = lane & 15, g = lane >> 4;
+
+  const int tiles_n = N / BN;
+  const int tn = blockIdx.x % tiles_n, tmi = blockIdx.x / tiles_n;
+  const int n0 = tn * BN, m0 = tmi * BM;
+  const int KB = K / kBK;
+
+  auto load_stage = [&](int kb, int buf) {
+    uint8_t* base = smem + buf * S::kStage;
+#pragma unroll
+    for (int j = 0; j < BM * 8 / S::kThreads; ++j) {
+      const int qi = j * S::kThreads + tid;
+      const int r = qi >> 3, p = qi & 7;
+      const int row = (m0 + r < M) ? m0 + r : M - 1;
+      g2lds16(A + static_cast<long>(row) * K + kb * kBK + ((p ^ swz(r)) << 4),
+              base + (j * S::kThreads + wave * 64) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < BN * 8 / S::kThreads; ++j) {
+      const int qi = j * S::kThreads + tid;
+      const int r = qi >> 3, p = qi & 7;
+      g2lds16(B + static_cast<long>(n0 + r) * K + kb * kBK + ((p ^ swz(r)) << 4),
+              base + S::kXBytes + (j * S::kThreads + wave * 64) * 16);
+    }
+    if constexpr (BLOCK) {
+      for (int j = wave; j < BM / 64; j += S::kThreads / 64) {
+        const int r = j * 64 + lane;
+        const int row = (m0 + r < M) ? m0 + r : M - 1;
+        g2lds4(sa + static_cast<long>(row) * KB + kb, base + S::kXBytes + S::kWBytes + j * 256);
+      }
+    }
+  };
+
+  v4f acc[S::kFW][S::kFT];
+#pragma unroll
+  for (int i = 0; i < S::kFW; ++i)
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  load_stage(0, 0);
+  for (int kb = 0; kb < KB; ++kb) {
+    const int buf = kb & 1;
+    wait_vm_all();
+    __syncthreads();
+    const uint8_t* xs = smem + buf * S::kStage;
+    const uint8_t* ws = xs + S::kXBytes;
+    v8i xr[S::kFT], wr[S::kFW];
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) xr[t] = load_frag_lds(xs, wm * S::kTM + 16 * t + lr, g);
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(ws, wn * S::kTN + 16 * i + lr, g);
+    float sab[S::kFT];
+    if constexpr (BLOCK) {
+      const float* sas = reinterpret_cast<const float*>(ws + S::kWBytes);
+      const float sw = sb[static_cast<long>((n0 + wn * S::kTN) / 128) * KB + kb];
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) sab[t] = sas[wm * S::kTM + 16 * t + lr] * sw;
+    }
+    if (kb + 1 < KB) load_stage(kb + 1, buf ^ 1);
+    Frag<E> xf[S::kFT];
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) xf[t] = prep<E>(xr[t]);
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i) {
+      const Frag<E> wf = prep<E>(wr[i]);
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) {
+        if constexpr (BLOCK) {
+          const v4f p = block_mma<E>(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
+        } else {
+          acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds weight rows n..n+3 of token m
+#pragma unroll
+  for (int t = 0; t < S::kFT; ++t) {
+    const int m = m0 + wm * S::kTM + 16 * t + lr;
+    if (m >= M) continue;
+    float sm = 1.0f;
+    if constexpr (!BLOCK) sm = sa[m];
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i) {
+      const int n = n0 + wn * S::kTN + 16 * i + 4 * g;
+      v4f v = acc[i][t];
+      if constexpr (!BLOCK) {
+        const float4 s4 = *reinterpret_cast<const float4*>(sb + n);
+        v[0] = v[0] * sm * s4.x;
+        v[1] = v[1] * sm * s4.y;
+        v[2] = v[2] * sm * s4.z;
+        v[3] = v[3] * sm * s4.w;
+      }
+      store_bf16x4(y + static_cast<long>(m) * N + n, v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------ skinny --
+template <int TMX, int RW, int WK, bool BLOCK, int E>
+__global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
+    uint16_t* __restrict__ y, float* __restrict__ ws, const uint8_t* __restrict__ A,
+    const float* __restrict__ sa, const uint8_t* __restrict__ B, const float* __restrict__ sb,
+    int M, int N, int K, int SPLIT) {
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [WK][RW*TMX][64] v4f
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * RW * 16;
+  const int s = blockIdx.y;
+  const int KB = K / kBK;
+  const int per = (KB + SPLIT - 1) / SPLIT;
+  const int kb_lo = s * per;
+  const int kb_hi = (kb_lo + per < KB) ? kb_lo + per : KB;
+
+  const uint8_t* wrow[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) wrow[i] = B + static_cast<long>(n0 + 16 * i + lr) * K + 32 * g;
+  const uint8_t* xrow[TMX];
+  bool xok[TMX];
+#pragma unroll
+  for (int t = 0; t < TMX; ++t) {
+    const int m = 16 * t + lr;
+    xok[t] = m < M;
+    xrow[t] = A + static_cast<long>(xok[t] ? m : 0) * K + 32 * g;
+  }
+  const long sb_row = static_cast<long>(n0 / 128) * KB;
+
+  v4f acc[RW][TMX];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int t = 0; t < TMX; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](const v8i* wr, const v8i* xr, const float* sab) {
+    Frag<E> xf[TMX];
+#pragma unroll
+    for (int t = 0; t < TMX; ++t) xf[t] = prep<E>(xr[t]);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const Frag<E> wf = prep<E>(wr[i]);
+#pragma unroll
+      for (int t = 0; t < TMX; ++t) {
+        if constexpr (BLOCK) {
+          const v4f p = block_mma<E>(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
+        } else {
+          acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
+        }
+      }
+    }
+  };
+  auto load = [&](int kb, v8i* wf, v8i* xf, float* sab) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) wf[i] = load_frag_global(wrow[i] + kb * kBK);
+#pragma unroll
+    for (int t = 0; t < TMX; ++t) {
+      if (xok[t]) {
+        xf[t] = load_frag_global(xrow[t] + kb * kBK);
+      } else {
+        xf[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    if constexpr (BLOCK) {
+      const float sw = sb[sb_row + kb];
+#pragma unroll
+      for (int t = 0; t < TMX; ++t)
+        sab[t] = xok[t] ? sa[static_cast<long>(16 * t + lr) * KB + kb] * sw : 0.0f;
+    }
+  };
+
+  int kb = kb_lo + wave;
+  for (; kb + WK < kb_hi; kb += 2 * WK) {
+    v8i wf0[RW], xf0[TMX], wf1[RW], xf1[TMX];
+    float sab0[TMX], sab1[TMX];
+    load(kb, wf0, xf0, sab0);
+    load(kb + WK, wf1, xf1, sab1);
+    step(wf0, xf0, sab0);
+    step(wf1, xf1, sab1);
+  }
+  if (kb < kb_hi) {
+    v8i wf0[RW], xf0[TMX];
+    float sab0[TMX];
+    load(kb, wf0, xf0, sab0);
+    step(wf0, xf0, sab0);
+  }
+
+  // reduce the WK waves' partial sums in a fixed order
+  constexpr int kFrags = RW * TMX;
+  if constexpr (WK > 1) {
+    v4f* r4 = reinterpret_cast<v4f*>(red);
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int t = 0; t < TMX; ++t) r4[(wave * kFrags + i * TMX + t) * 64 + lane] = acc[i][t];
+    __syncthreads();
+  }
+  for (int f = (WK > 1 ? wave : 0); f < kFrags; f += WK) {
+    const int i = f / TMX, t = f % TMX;
+    v4f v;
+    if constexpr (WK > 1) {
+      const v4f* r4 = reinterpret_cast<const v4f*>(red);
+      v = r4[f * 64 + lane];
+      for (int w = 1; w < WK; ++w) v += r4[(w * kFrags + f) * 64 + lane];
+    } else {
+      v = acc[i][t];
+    }
+    const int m = 16 * t + lr;
+    if (m >= M) continue;
+    const int n = n0 + 16 * i + 4 * g;
+    if (SPLIT > 1) {
+      *reinterpret_cast<v4f*>(ws + (static_cast<long>(s) * M + m) * N + n) = v;
+      continue;
+    }
+    if constexpr (!BLOCK) {
+      const float sm = sa[m];
+      const float4 s4 = *reinterpret_cast<const float4*>(sb + n);
+      v[0] = v[0] * sm * s4.x;
+      v[1] = v[1] * sm * s4.y;
+      v[2] = v[2] * sm * s4.z;
+      v[3] = v[3] * sm * s4.w;
+    }
+    store_bf16x4(y + static_cast<long>(m) * N + n, v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Ordered sum of the split-K partials, then (scaled_mm) the epilogue scales.
+template <bool BLOCK>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict__ y,
+                                                            const float* __restrict__ ws,
+                                                            const float* __restrict__ sa,
+                                                            const float* __restrict__ sb,
+                                                            int M, int N, int SPLIT) {
+  const long total = static_cast<long>(M) * (N / 4);
+  for (long idx = blockIdx.x * 256L + threadIdx.x; idx < total; idx += gridDim.x * 256L) {
+    const int m = static_cast<int>(idx / (N / 4));
+    const int n = static_cast<int>(idx % (N / 4)) * 4;
+    float4 v = *reinterpret_cast<const float4*>(ws + static_cast<long>(m) * N + n);
+    for (int s = 1; s < SPLIT; ++s) {
+      const float4 u = *reinterpret_cast<const float4*>(ws + (static_cast<long>(s) * M + m) * N + n);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    if constexpr (!BLOCK) {
+      const float sm = sa[m];
+      const float4 s4 = *reinterpret_cast<const float4*>(sb + n);
+      v.x = v.x * sm * s4.x;
+      v.y = v.y * sm * s4.y;
+      v.z = v.z * sm * s4.z;
+      v.w = v.w * sm * s4.w;
+    }
+    store_bf16x4(y + static_cast<long>(m) * N + n, v.x, v.y, v.z, v.w);
+  }
+}
+
+// ------------------------------------------------------ registry --
+struct Variant {
+  GemmConfig cfg;
+  const void* fn[2];  // [blockwise]
+  int threads;
+  size_t lds;
+};
+
+// Variant names live as long as the process (the registry is never freed).
+const char* keep_name(const std::string& n) {
+  static std::mutex mu;
+  static std::vector<std::unique_ptr<std::string>> names;
+  std::lock_guard<std::mutex> lock(mu);
+  names.push_back(std::make_unique<std::string>(n));
+  return names.back()->c_str();
+}
+
+template <int BM, int BN, int WM, int WN, int E>
+Variant tiled_variant() {
+  Variant v{};
+  const char* name = keep_name(std::string(E == kEngineF8 ? "f8" : "f16") + "_tiled_m" +
+                               std::to_string(BM) + "_n" + std::to_string(BN) + "_w" +
+                               std::to_string(WM) + "x" + std::to_string(WN));
+  v.cfg = GemmConfig{name, kTiled, E, BM, BN, WM, WN, 0, 0, 0, 1};
+  v.fn[0] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, false, E>);
+  v.fn[1] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, true, E>);
+  v.threads = WM * WN * 64;
+  v.lds = TiledShape<BM, BN, WM, WN, true>::kLds;  // the larger of the two
+  return v;
+}
+
+template <int TMX, int RW, int WK, int E>
+Variant skinny_variant(int split) {
+  Variant v{};
+  const char* name = keep_name(std::string(E == kEngineF8 ? "f8" : "f16") + "_skinny_t" +
+                               std::to_string(TMX) + "_r" + std::to_string(RW) + "_k" +
+                               std::to_string(WK) + "_s" + std::to_string(split));
+  v.cfg = GemmConfig{name, kSkinny, E, 0, 0, 0, 0, TMX, RW, WK, split};
+  v.fn[0] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, false, E>);
+  v.fn[1] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, true, E>);
+  v.threads = WK * 64;
+  v.lds = WK > 1 ? static_cast<size_t>(WK) * RW * TMX * 64 * 16 : 0;
+  return v;
+}
+
+std::vector<Variant>& registry() {
+  static std::vector<Variant> r = [] {
+    std::vector<Variant> v;
+    v.push_back(tiled_variant<128, 128, 2, 2, kEngineF16>());
+    v.push_back(tiled_variant<256, 128, 2, 2, kEngineF16>());
+    v.push_back(tiled_variant<128, 256, 2, 4, kEngineF16>());
+    v.push_back(tiled_variant<64, 128, 1, 2, kEngineF16>());
+    v.push_back(tiled_variant<128, 128, 2, 2, kEngineF8>());
+    v.push_back(tiled_variant<256, 128, 2, 2, kEngineF8>());
+    v.push_back(tiled_variant<128, 256, 2, 4, kEngineF8>());
+    v.push_back(tiled_variant<64, 128, 1, 2, kEngineF8>());
+#define FP8Q_SKINNY(T, R, W) \
+  for (int s : {1, 2, 4, 8}) v.push_back(skinny_variant<T, R, W, kEngineF16>(s));
+    FP8Q_SKINNY(1, 1, 4)
+    FP8Q_SKINNY(1, 1, 8)
+    FP8Q_SKINNY(1, 2, 4)
+    FP8Q_SKINNY(1, 2, 8)
+    FP8Q_SKINNY(1, 4, 4)
+    FP8Q_SKINNY(1, 4, 8)
+    FP8Q_SKINNY(2, 1, 4)
+    FP8Q_SKINNY(2, 1, 8)
+    FP8Q_SKINNY(2, 2, 4)
+    FP8Q_SKINNY(2, 2, 8)
+    FP8Q_SKINNY(2, 4, 4)
+    FP8Q_SKINNY(2, 4, 8)
+    FP8Q_SKINNY(4, 1, 4)
+    FP8Q_SKINNY(4, 1, 8)
+    FP8Q_SKINNY(4, 2, 4)
+    FP8Q_SKINNY(4, 2, 8)
+    FP8Q_SKINNY(4, 4, 4)
+    FP8Q_SKINNY(8, 1, 4)
+    FP8Q_SKINNY(8, 1, 8)
+    FP8Q_SKINNY(8, 2, 4)
+#undef FP8Q_SKINNY
+    return v;
+  }();
+  return r;
+}
+
+// Raise the dynamic-LDS limit of each kernel once (above 64 KiB needs it).
+void ensure_lds_attr(const Variant& v, int blockwise) {
+  static std::mutex mu;
+  static std::vector<const void*> done;
+  const void* fn = v.fn[blockwise];
+  std::lock_guard<std::mutex> lock(mu);
+  for (const void* d : done)
+    if (d == fn) return;
+  if (v.lds > 64 * 1024)
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(v.lds));
+  done.push_back(fn);
+}
+
+}  // namespace
+
+int gemm_num_configs() { return static_cast<int>(registry().size()); }
+const GemmConfig& gemm_config(int id) { return registry()[id].cfg; }
+
+bool gemm_config_fits(int id, long M, long N, long K) {
+  const GemmConfig& c = gemm_config(id);
+  if (c.kind == kTiled) return N % c.bn == 0;
+  if (M > 16L * c.tm) return false;
+  if (N % (16L * c.rw)) return false;
+  return true;
+}
+
+size_t gemm_workspace_bytes(int id, long M, long N, long K) {
+  const GemmConfig& c = gemm_config(id);
+  if (c.kind != kSkinny || c.split <= 1) return 0;
+  return static_cast<size_t>(c.split) * M * N * sizeof(float);
+}
+
+hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, const float* sa,
+                       const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
+                       hipStream_t st) {
+  const Variant& v = registry()[id];
+  const int bw = blockwise ? 1 : 0;
+  ensure_lds_attr(v, bw);
+  if (v.cfg.kind == kTiled) {
+    const int tiles = (N / v.cfg.bn) * ((M + v.cfg.bm - 1) / v.cfg.bm);
+    void* args[] = {&y, &a, &sa, &b, &sb, &M, &N, &K};
+    return hipLaunchKernel(v.fn[bw], dim3(tiles), dim3(v.threads), args, v.lds, st);
+  }
+  int split = v.cfg.split;
+  float* wsf = static_cast<float*>(ws);
+  {
+    void* args[] = {&y, &wsf, &a, &sa, &b, &sb, &M, &N, &K, &split};
+    hipError_t e0 = hipLaunchKernel(v.fn[bw], dim3(N / (16 * v.cfg.rw), split), dim3(v.threads),
+                                    args, v.lds, st);
+    if (e0 != hipSuccess) return e0;
+  }
+  if (split <= 1) return hipSuccess;
+  const long total = static_cast<long>(M) * (N / 4);
+  long blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blockwise)
+    hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(blocks), dim3(256), 0, st, y, wsf, sa,
+                       sb, M, N, split);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(blocks), dim3(256), 0, st, y, wsf, sa,
+                       sb, M, N, split);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

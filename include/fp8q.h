@@ -1,0 +1,189 @@
+/*
+ * fp8q -- the FP8 quantized linear layer of LLM inference on AMD Instinct
+ * MI355X (gfx950): fused RMSNorm / SiLU-and-mul + dynamic FP8 quantization,
+ * and the per-token and block-scaled FP8 GEMMs.
+ *
+ * The operations are the ones named on the page "Helion in vLLM: FP8
+ * inference of Qwen3" (24-ai.news, 2026-06-10), section "Kernels integrated
+ * into vLLM": rms_norm_dynamic_per_token_quant, rms_norm_per_block_quant,
+ * silu_and_mul_dynamic_per_token_quant, silu_and_mul_per_block_quant,
+ * dynamic_per_token_scaled_fp8_quant, per_token_group_fp8_quant, scaled_mm and
+ * scaled_mm_blockwise.  The small-M split-K and swap-AB GEMM regimes follow
+ * the page "Helion can accelerate vLLM LLM inference on NVIDIA GPUs"
+ * (aihirek.info), section "One GEMM implementation handles several
+ * algorithms"; the choice among them is a per-shape table (same page,
+ * section "Autotuning picks the right variant").
+ *
+ * Formats (the pages say only "FP8"; these are the readings adopted):
+ *   FP8   OCP e4m3 ("e4m3fn"): bias 7, max 448, no infinity, NaN 0x7F/0xFF.
+ *   bf16  IEEE binary32 truncated to 16 bits, stored as uint16.
+ *   scale fp32, scale = amax / 448 (IEEE division), q = e4m3(RN32(y / scale)),
+ *         an all-zero group gets scale 0 and signed-zero codes.
+ *   group 1 x 128 consecutive elements of a row; weight blocks 128 x 128.
+ *
+ * Conventions for every entry point
+ *   - Outputs first, then inputs, then sizes and scalars, then the stream.
+ *   - All pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or synchronizes, and keeps no state between calls.
+ *   - All tensors are dense and row-major (no strides).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; a successful return means the
+ *     kernels were launched, not that they finished.
+ *   - Arguments are checked on the host before any HIP call; a violation
+ *     returns an error status and launches nothing.  M == 0 is a no-op that
+ *     returns FP8Q_OK (pointers are then not inspected).
+ *   - Every pointer must be 16-byte aligned.
+ *   - Inputs must be finite; NaN or infinity in inputs is outside the
+ *     contract (no fault, unspecified values).
+ *   - Functions are reentrant; calls on one stream are ordered by the stream.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_VERSION 100 /* major*100 + minor */
+
+typedef enum {
+  FP8Q_OK = 0,
+  FP8Q_ERR_INVALID_ARG = 1,       /* null pointer, negative size, bad eps */
+  FP8Q_ERR_UNSUPPORTED_SHAPE = 2, /* size not a multiple the op needs     */
+  FP8Q_ERR_ALIGNMENT = 3,         /* a pointer is not 16-byte aligned     */
+  FP8Q_ERR_WORKSPACE = 4,         /* ws smaller than fp8q_workspace_size  */
+  FP8Q_ERR_NO_DEVICE = 5,         /* no HIP device is usable              */
+  FP8Q_ERR_ARCH = 6,              /* current device is not gfx950         */
+  FP8Q_ERR_HIP = 7,               /* a HIP call failed, see last_hip_error*/
+  FP8Q_ERR_BAD_MODE = 8,          /* unknown quantization mode            */
+  FP8Q_ERR_BAD_CONFIG = 9         /* unknown or inapplicable GEMM config  */
+} fp8q_status;
+
+typedef enum {
+  FP8Q_PER_TOKEN = 0, /* one scale per row:       scale [M]         */
+  FP8Q_GROUP128 = 1   /* one scale per 1x128:     scale [M, K/128]  */
+} fp8q_quant_mode;
+
+typedef enum { FP8Q_OP_SCALED_MM = 0, FP8Q_OP_SCALED_MM_BLOCKWISE = 1 } fp8q_gemm_op;
+
+/* ------------------------------------------------------------------------
+ * Fused RMSNorm + dynamic FP8 quantization
+ * (rms_norm_dynamic_per_token_quant / rms_norm_per_block_quant).
+ *
+ *   inv  = RN32(1 / sqrt(sum_k x[m,k]^2 / K + eps))   sum in fp64, the rest
+ *                                                      in IEEE fp64
+ *   y    = RN32(RN32(x[m,k] * w[k]) * inv)             no bf16 rounding of y
+ *   then the quantizer per row (PER_TOKEN) or per 1x128 group (GROUP128).
+ *
+ *   q     [M, K]   e4m3 bytes            (out)
+ *   scale [M] or [M, K/128] fp32         (out)
+ *   x     [M, K]   bf16                  (in)
+ *   w     [K]      bf16                  (in)
+ *   eps   > 0, finite
+ * Needs K > 0, K % 8 == 0 (PER_TOKEN) or K % 128 == 0 (GROUP128),
+ * K <= 65536.
+ * ---------------------------------------------------------------------- */
+int fp8q_rmsnorm_quant(void* q, float* scale, const void* x, const void* w, int64_t M,
+                       int64_t K, float eps, int mode, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused SiLU-and-mul + dynamic FP8 quantization
+ * (silu_and_mul_dynamic_per_token_quant / silu_and_mul_per_block_quant).
+ *
+ *   y[m,d] = RN32(silu(gate_up[m,d]) * gate_up[m,D+d]),  silu correctly
+ *            rounded to fp32; then the quantizer as above.
+ *
+ *   q       [M, D]   e4m3 bytes           (out)
+ *   scale   [M] or [M, D/128] fp32        (out)
+ *   gate_up [M, 2D]  bf16, gate = columns [0,D), up = [D,2D)   (in)
+ * Needs D > 0, D % 8 == 0 (PER_TOKEN) or D % 128 == 0 (GROUP128),
+ * D <= 65536.
+ * ---------------------------------------------------------------------- */
+int fp8q_silu_mul_quant(void* q, float* scale, const void* gate_up, int64_t M, int64_t D,
+                        int mode, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Standalone dynamic FP8 quantization of a bf16 matrix
+ * (dynamic_per_token_scaled_fp8_quant / per_token_group_fp8_quant):
+ * the quantizer with an identity front end.  Arguments as for
+ * fp8q_rmsnorm_quant without w and eps.
+ * ---------------------------------------------------------------------- */
+int fp8q_quant(void* q, float* scale, const void* x, int64_t M, int64_t K, int mode,
+               void* stream);
+
+/* ------------------------------------------------------------------------
+ * scaled_mm: per-token x per-channel scaled FP8 GEMM, "NT" layout.
+ *
+ *   y[m,n] = bf16( sa[m] * sb[n] * sum_k a[m,k] * b[n,k] )   fp32 accumulate
+ *
+ *   y  [M, N] bf16 (out)     a [M, K] e4m3 (in)   b [N, K] e4m3 (in)
+ *   sa [M] fp32 (in)         sb [N] fp32 (in)
+ *   ws / ws_bytes: device workspace of at least
+ *                  fp8q_workspace_size(FP8Q_OP_SCALED_MM, M, N, K) bytes;
+ *                  may be NULL when that size is 0.
+ * Needs K % 128 == 0, N % 128 == 0, K > 0, N > 0.
+ * ---------------------------------------------------------------------- */
+int fp8q_scaled_mm(void* y, const void* a, const void* b, const float* sa, const float* sb,
+                   int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * scaled_mm_blockwise: 1x128 activation x 128x128 weight block-scaled GEMM.
+ *
+ *   y[m,n] = bf16( sum_kb sa[m,kb] * sb[n/128,kb]
+ *                          * sum_{k in block kb} a[m,k] * b[n,k] )
+ *   products inside a 128-block are summed in fp32 before its scales apply.
+ *
+ *   y  [M, N] bf16 (out)    a [M, K] e4m3 (in)     sa [M, K/128] fp32 (in)
+ *   b  [N, K] e4m3 (in)     sb [N/128, K/128] fp32 (in)
+ *   ws / ws_bytes as for fp8q_scaled_mm (op FP8Q_OP_SCALED_MM_BLOCKWISE).
+ * Needs K % 128 == 0, N % 128 == 0, K > 0, N > 0.
+ * ---------------------------------------------------------------------- */
+int fp8q_scaled_mm_blockwise(void* y, const void* a, const float* sa, const void* b,
+                             const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Bytes of workspace the GEMM `op` needs for this shape with the table's
+ * choice (0 when the chosen variant needs none).  Pure host function. */
+size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------
+ * GEMM variants.  The same two GEMMs with the variant forced instead of
+ * taken from the per-shape table; used by tests (every variant is checked)
+ * and by the table's tuner.  cfg < 0 means "use the table".
+ * Returns FP8Q_ERR_BAD_CONFIG when cfg is unknown or cannot run this shape.
+ * ---------------------------------------------------------------------- */
+int fp8q_gemm_num_configs(void);
+const char* fp8q_gemm_config_name(int cfg);
+int fp8q_gemm_config_for(int op, int64_t M, int64_t N, int64_t K); /* table lookup */
+size_t fp8q_workspace_size_cfg(int cfg, int64_t M, int64_t N, int64_t K);
+int fp8q_scaled_mm_cfg(void* y, const void* a, const void* b, const float* sa,
+                       const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                       size_t ws_bytes, int cfg, void* stream);
+int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const float* sa, const void* b,
+                                 const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                                 size_t ws_bytes, int cfg, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Elementwise building blocks (also used to test the device arithmetic
+ * exhaustively).
+ *   fp8q_cvt_e4m3: q[i] = e4m3(x[i]) for fp32 x, round to nearest even,
+ *                  saturating to +-448, sign of zero kept.
+ *   fp8q_silu:     y[i] = fp32 silu(g[i]) correctly rounded, g bf16.
+ * n >= 0; n == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+int fp8q_cvt_e4m3(void* q, const float* x, int64_t n, void* stream);
+int fp8q_silu(float* y, const void* g, int64_t n, void* stream);
+
+/* Diagnostics. */
+const char* fp8q_status_string(int status);
+int fp8q_last_hip_error(void); /* hipError_t of this thread's last FP8Q_ERR_HIP */
+int fp8q_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8Q_H */

@@ -1,0 +1,150 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before touching any device.
+
+Pointers passed here are fake (never dereferenced): every call either fails
+validation on the host, or -- only where no GPU is present -- stops at the
+device check with FP8Q_ERR_NO_DEVICE.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_block_scaled_rms_amd as fq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fp8q.h")
+
+OK, INVALID, SHAPE, ALIGN, WS, NODEV, ARCH, HIP, MODE, CFG = range(10)
+
+A, B, C, D, E = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000  # 16-byte aligned fakes
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text)))
+
+
+def _no_gpu():
+    return torch.cuda.device_count() == 0
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fq.LIB_PATH)
+    names = _declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the binding declares a signature for each of them
+    assert set(names) == set(fq.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    L = fq.lib()
+    assert L.fp8q_version() == 100
+    for s in range(10):
+        assert L.fp8q_status_string(s)
+    assert L.fp8q_status_string(99) == b"unknown status"
+
+
+def test_quant_argument_checks():
+    L = fq.lib()
+    rms = L.fp8q_rmsnorm_quant
+    assert rms(A, B, C, D, -1, 256, 1e-6, 1, None) == INVALID
+    assert rms(A, B, C, D, 4, 0, 1e-6, 1, None) == INVALID
+    assert rms(A, B, C, D, 4, 256, 1e-6, 2, None) == MODE
+    assert rms(A, B, C, D, 0, 256, 1e-6, 1, None) == OK          # M == 0: no-op
+    assert rms(0, 0, 0, 0, 0, 256, 1e-6, 1, None) == OK          # not inspected
+    assert rms(0, B, C, D, 4, 256, 1e-6, 1, None) == INVALID
+    assert rms(A, B, C, 0, 4, 256, 1e-6, 1, None) == INVALID
+    assert rms(A + 8, B, C, D, 4, 256, 1e-6, 1, None) == ALIGN
+    assert rms(A, B, C, D + 2, 4, 256, 1e-6, 1, None) == ALIGN
+    assert rms(A, B, C, D, 4, 200, 1e-6, 1, None) == SHAPE       # K % 128 (group)
+    assert rms(A, B, C, D, 4, 12, 1e-6, 0, None) == SHAPE        # K % 8 (per token)
+    assert rms(A, B, C, D, 4, 65536, 1e-6, 0, None) == SHAPE     # K too large
+    assert rms(A, B, C, D, 4, 256, 0.0, 1, None) == INVALID      # eps
+    assert rms(A, B, C, D, 4, 256, float("inf"), 1, None) == INVALID
+    assert rms(A, B, C, D, 4, 256, float("nan"), 1, None) == INVALID
+    silu = L.fp8q_silu_mul_quant
+    assert silu(A, B, C, 4, 0, 1, None) == INVALID
+    assert silu(A, B, C, 4, 100, 1, None) == SHAPE
+    assert silu(A, B, C + 4, 4, 128, 1, None) == ALIGN
+    assert silu(A, B, C, 4, 128, 7, None) == MODE
+    q = L.fp8q_quant
+    assert q(A, B, C, 4, 136, 1, None) == SHAPE
+    assert q(A, 0, C, 4, 128, 1, None) == INVALID
+
+
+def test_gemm_argument_checks():
+    L = fq.lib()
+    mm = L.fp8q_scaled_mm
+    bw = L.fp8q_scaled_mm_blockwise
+    assert mm(A, B, C, D, E, 0, 256, 256, None, 0, None) == OK
+    assert mm(A, B, C, D, E, -1, 256, 256, None, 0, None) == INVALID
+    assert mm(A, B, C, D, E, 4, 200, 256, None, 0, None) == SHAPE
+    assert mm(A, B, C, D, E, 4, 256, 100, None, 0, None) == SHAPE
+    assert mm(A, B, C, D, E, 4, 0, 256, None, 0, None) == INVALID
+    assert mm(A + 2, B, C, D, E, 4, 256, 256, None, 0, None) == ALIGN
+    assert bw(A, B, C, D, 0, 4, 256, 256, None, 0, None) == INVALID
+    assert bw(A, B, C, D, E + 4, 4, 256, 256, None, 0, None) == ALIGN
+    # forced variants
+    n = L.fp8q_gemm_num_configs()
+    assert n > 4
+    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 4, 256, 256, None, 0, n, None) == CFG
+    # a skinny variant cannot take more tokens than its fragment count
+    sk = next(i for i in range(n) if "_skinny_t1_" in fq.fp8q_gemm_config_name(i))
+    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 17, 256, 256, None, 0, sk, None) == CFG
+    # split-K variant without a workspace
+    sp = next(i for i in range(n) if fq.fp8q_gemm_config_name(i).endswith("_s4"))
+    need = L.fp8q_workspace_size_cfg(sp, 8, 256, 1024)
+    assert need == 4 * 8 * 256 * 4
+    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 1024, None, 0, sp, None) == WS
+    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 1024, A, need - 1, sp, None) == WS
+
+
+def test_elementwise_argument_checks():
+    L = fq.lib()
+    assert L.fp8q_cvt_e4m3(A, B, 0, None) == OK
+    assert L.fp8q_cvt_e4m3(A, B, -1, None) == INVALID
+    assert L.fp8q_cvt_e4m3(0, B, 5, None) == INVALID
+    assert L.fp8q_silu(A, B + 2, 5, None) == ALIGN
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device path; a GPU is present")
+def test_valid_calls_report_no_device_without_gpu():
+    L = fq.lib()
+    assert L.fp8q_rmsnorm_quant(A, B, C, D, 4, 256, 1e-6, 1, None) == NODEV
+    assert L.fp8q_silu_mul_quant(A, B, C, 4, 128, 0, None) == NODEV
+    assert L.fp8q_quant(A, B, C, 4, 128, 1, None) == NODEV
+    assert L.fp8q_scaled_mm(A, B, C, D, E, 4, 256, 256, None, 0, None) == NODEV
+    assert L.fp8q_scaled_mm_blockwise(A, B, C, D, E, 4, 256, 256, None, 0, None) == NODEV
+    assert L.fp8q_cvt_e4m3(A, B, 16, None) == NODEV
+    assert L.fp8q_silu(A, B, 16, None) == NODEV
+
+
+def test_dispatch_table_covers_every_workload_shape():
+    """Every GEMM shape of the Qwen3 workloads resolves to a variant that can
+    run it, and the workspace query agrees with that variant."""
+    shapes = []
+    for M in (1, 16, 128, 512, 2048):
+        for N, K in ((4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144)):
+            shapes.append((0, M, N, K))
+    for M in (1, 2, 4, 8, 16, 32):
+        for N, K in ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)):
+            shapes.append((1, M, N, K))
+    for M in (2048, 8192):
+        for N, K in ((10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)):
+            shapes.append((1, M, N, K))
+    for M in (64, 4096):
+        shapes.append((1, M, 5120, 25600))
+    shapes.append((1, 16, 512, 256))
+    for op, M, N, K in shapes:
+        cfg = fq.fp8q_gemm_config_for(op, M, N, K)
+        assert cfg >= 0, (op, M, N, K)
+        assert fq.fp8q_workspace_size(op, M, N, K) == fq.fp8q_workspace_size(op, M, N, K, cfg)
+        name = fq.fp8q_gemm_config_name(cfg)
+        assert name.startswith("f16_"), name  # the default is the exact engine
+        if "_skinny_t" in name:
+            assert M <= 16 * int(name.split("_skinny_t")[1].split("_")[0])

@@ -1,0 +1,255 @@
+"""GPU parity of the FP8 GEMMs against the CPU oracle.
+
+* Every compiled variant (tiled, skinny, every split-K factor) on a ragged
+  shape, for both scaled_mm and scaled_mm_blockwise: the oracle acceptance
+  rule on random codes, and exact bf16 results on one-hot weights with
+  power-of-two scales (each output is then a single exactly representable
+  product, so any misplaced element, row, column or block scale shows).
+* The table's choice at every Qwen3 workload shape: full comparison where
+  the oracle is quick, sampled rows at the largest sizes.
+* Determinism and guard bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_rms_amd as fq
+import synth
+from oracle import e4m3, gemm, quant
+from gpu_util import DEV, bf16_dev, bf16_host, bf16_host_f64, f32_dev, host, say, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+MM, BW = fq.OP_SCALED_MM, fq.OP_SCALED_MM_BLOCKWISE
+
+
+def _configs():
+    return [(i, fq.fp8q_gemm_config_name(i)) for i in range(fq.fp8q_gemm_num_configs())]
+
+
+def _fp8_engine_bound(op, a, sa, b, sb):
+    """Error bound of the FP8-MFMA engine (variants named f8_*), derived from
+    its measured arithmetic: inside each group of 8 consecutive K the
+    datapath truncates every product to a multiple of 2^(E-13), E the
+    exponent of the group's largest |product|; everything else is fp32.
+    Returns the bound on |out - ref| before the bf16 output rounding."""
+    A = e4m3.decode(a)
+    B = e4m3.decode(b)
+    M, K = A.shape
+    N = B.shape[0]
+    bound = np.zeros((M, N))
+    for kb in range(K // 128):
+        blk = np.zeros((M, N))
+        for g in range(16):
+            ks = slice(kb * 128 + 8 * g, kb * 128 + 8 * g + 8)
+            pmax = np.max(np.abs(A[:, None, ks] * B[None, :, ks]), axis=2)
+            e = np.floor(np.log2(np.where(pmax > 0, pmax, 1.0)))
+            blk += np.where(pmax > 0, 7.0 * np.exp2(e - 13), 0.0)
+        if op == MM:
+            bound += blk
+        else:
+            bound += blk * sa[:, kb][:, None].astype(np.float64) * np.repeat(
+                sb[:, kb], 128)[None, :].astype(np.float64)
+    if op == MM:
+        bound *= sa[:, None].astype(np.float64) * sb[None, :].astype(np.float64)
+    return bound
+
+
+def _check_engine(name, op, y, a, sa, b, sb):
+    ref = _ref(op, a, sa, b, sb)
+    out = bf16_host_f64(y)
+    if name.startswith("f16_"):
+        res = gemm.acceptance(out, ref)
+        assert res["ok"], res
+        return
+    # FP8-MFMA engine: within bf16 rounding + fp32 slack of the hardware bound
+    bound = _fp8_engine_bound(op, a, sa, b, sb)
+    mag = _ref(op, a & 0x7F, sa, b & 0x7F, sb)  # sum of |terms|
+    slack = 2.0 ** -8 * np.abs(ref) + bound * 1.001 + 2.0 ** -20 * mag + 1e-30
+    bad = np.abs(out - ref) > slack
+    assert not bad.any(), (int(bad.sum()), float(np.max(np.abs(out - ref) / slack)))
+    assert gemm.acceptance(out, ref)["rel_fro"] <= gemm.REL_FRO_TOL
+
+
+def _m_for(name):
+    if "_skinny_t" in name:
+        return 16 * int(name.split("_skinny_t")[1].split("_")[0]) - 3
+    return 200
+
+
+def _run(op, a, sa, b, sb, cfg=None):
+    at, bt = u8_dev(a), u8_dev(b)
+    sat, sbt = f32_dev(sa), f32_dev(sb)
+    if op == MM:
+        y = fq.scaled_mm(at, bt, sat, sbt, cfg=cfg)
+    else:
+        y = fq.scaled_mm_blockwise(at, sat, bt, sbt, cfg=cfg)
+    torch.cuda.synchronize()
+    return y
+
+
+def _ref(op, a, sa, b, sb):
+    return gemm.scaled_mm(a, b, sa, sb) if op == MM else gemm.scaled_mm_blockwise(a, sa, b, sb)
+
+
+def _scales(rng, op, M, N, K, pow2=False):
+    if op == MM:
+        shp_a, shp_b = (M,), (N,)
+    else:
+        shp_a, shp_b = (M, K // 128), (N // 128, K // 128)
+    if pow2:
+        return (np.exp2(rng.integers(-6, 3, shp_a)).astype(np.float32),
+                np.exp2(rng.integers(-6, 3, shp_b)).astype(np.float32))
+    return synth.gen_scales(rng, shp_a), synth.gen_scales(rng, shp_b)
+
+
+@pytest.mark.parametrize("op", [MM, BW], ids=["mm", "blockwise"])
+@pytest.mark.parametrize("cfg,name", _configs(), ids=[n for _, n in _configs()])
+def test_every_variant_random(cfg, name, op):
+    M, N, K = _m_for(name), 256, 1024
+    say("gemm variant random", name, op, M, N, K)
+    rng = synth.rng_for("variant", name, op, M, N, K)
+    a = synth.gen_e4m3_codes(rng, (M, K))
+    b = synth.gen_e4m3_codes(rng, (N, K))
+    sa, sb = _scales(rng, op, M, N, K)
+    y = _run(op, a, sa, b, sb, cfg)
+    _check_engine(name, op, y, a, sa, b, sb)
+
+
+@pytest.mark.parametrize("op", [MM, BW], ids=["mm", "blockwise"])
+@pytest.mark.parametrize("cfg,name", _configs(), ids=[n for _, n in _configs()])
+def test_every_variant_one_hot_exact(cfg, name, op):
+    M, N, K = _m_for(name), 256, 1024
+    say("gemm variant one-hot", name, op, M, N, K)
+    rng = synth.rng_for("onehot", name, op, M, N, K)
+    a = synth.gen_e4m3_codes(rng, (M, K))
+    perm = rng.permutation(K)[:N]
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), perm] = 0x38  # 1.0
+    sa, sb = _scales(rng, op, M, N, K, pow2=True)
+    y = bf16_host_f64(_run(op, a, sa, b, sb, cfg))
+    ref = _ref(op, a, sa, b, sb)  # exactly representable in bf16 here
+    assert np.array_equal(y, ref)
+
+
+def _gemm_case(config, op, M, N, K, realistic):
+    rng = synth.rng_for(config, "gemm", op, M, N, K)
+    if realistic:
+        x = synth.gen_activations(rng, M, K)
+        a, sa = quant.quantize(x, quant.PER_TOKEN if op == MM else quant.GROUP128)
+        W = synth.gen_linear_weight(rng, N, K)
+        b, sb = quant.quant_weight_per_channel(W) if op == MM else quant.quant_weight_block128(W)
+    else:
+        a = synth.gen_e4m3_codes(rng, (M, K))
+        b = synth.gen_e4m3_codes(rng, (N, K))
+        sa, sb = _scales(rng, op, M, N, K)
+    return a, sa, b, sb
+
+
+C2 = [(M, N, K) for M in (1, 16, 128, 512) for N, K in ((4096, 2048), (2048, 2048),
+                                                         (12288, 2048), (2048, 6144))]
+C3 = [(M, N, K) for M in (1, 2, 4, 8, 16, 32) for N, K in ((6144, 4096), (4096, 4096),
+                                                            (24576, 4096), (4096, 12288))]
+
+
+@pytest.mark.parametrize("M,N,K", C2)
+def test_scaled_mm_qwen3_1p7b_shapes(M, N, K):
+    say("scaled_mm c2", M, N, K, fq.fp8q_gemm_config_name(fq.fp8q_gemm_config_for(MM, M, N, K)))
+    a, sa, b, sb = _gemm_case("c2", MM, M, N, K, realistic=True)
+    y = _run(MM, a, sa, b, sb)
+    res = gemm.acceptance(bf16_host_f64(y), gemm.scaled_mm(a, b, sa, sb))
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("M,N,K", C3)
+def test_blockwise_qwen3_8b_decode_shapes(M, N, K):
+    say("blockwise c3", M, N, K, fq.fp8q_gemm_config_name(fq.fp8q_gemm_config_for(BW, M, N, K)))
+    a, sa, b, sb = _gemm_case("c3", BW, M, N, K, realistic=(N * K <= 4096 * 4096))
+    y = _run(BW, a, sa, b, sb)
+    res = gemm.acceptance(bf16_host_f64(y), gemm.scaled_mm_blockwise(a, sa, b, sb))
+    assert res["ok"], res
+
+
+def _sampled_rows(M, n):
+    rng = np.random.default_rng(M + 7)
+    return np.sort(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), n - 2, False)]))
+
+
+LARGE = [
+    (MM, 2048, 4096, 2048), (MM, 2048, 2048, 2048), (MM, 2048, 12288, 2048),
+    (MM, 2048, 2048, 6144),
+    (BW, 2048, 10240, 5120), (BW, 2048, 5120, 8192), (BW, 2048, 51200, 5120),
+    (BW, 2048, 5120, 25600),
+    (BW, 8192, 10240, 5120), (BW, 8192, 5120, 8192), (BW, 8192, 51200, 5120),
+    (BW, 8192, 5120, 25600),
+    (BW, 64, 5120, 25600), (BW, 4096, 5120, 25600),
+]
+
+
+@pytest.mark.parametrize("op,M,N,K", LARGE)
+def test_large_shapes_sampled_rows(op, M, N, K):
+    """Full-size Qwen3 prefill / MLP-tail shapes in the table's launch
+    configuration; 48 sampled rows (all columns) against the oracle."""
+    say("gemm large", op, M, N, K, fq.fp8q_gemm_config_name(fq.fp8q_gemm_config_for(op, M, N, K)))
+    a, sa, b, sb = _gemm_case("large", op, M, N, K, realistic=False)
+    y = _run(op, a, sa, b, sb)
+    rows = _sampled_rows(M, 48) if M > 48 else np.arange(M)
+    ya = bf16_host_f64(y[torch.from_numpy(rows).to(DEV)])
+    ref = _ref(op, a[rows], sa[rows], b, sb)
+    res = gemm.acceptance(ya, ref)
+    assert res["ok"], res
+
+
+def test_c1_tiny_pipeline_end_to_end():
+    """rmsnorm_quant (group128) -> scaled_mm_blockwise on the tiny blockwise
+    workload (M=16, K=256, N=512), against the oracle pipeline."""
+    M, K, N = 16, 256, 512
+    rng = synth.rng_for("c1", M, N, K)
+    x = synth.gen_activations(rng, M, K, outlier_frac=0.0)
+    w = synth.gen_rms_weight(rng, K)
+    W = synth.gen_linear_weight(rng, N, K)
+    b, sb = quant.quant_weight_block128(W)
+    q, s = fq.rmsnorm_quant(bf16_dev(x), bf16_dev(w), 1e-6, fq.GROUP128)
+    y = fq.scaled_mm_blockwise(q, s, u8_dev(b), f32_dev(sb))
+    torch.cuda.synchronize()
+    qr, sr = quant.rmsnorm_quant(x, w, 1e-6, quant.GROUP128)
+    assert np.array_equal(host(q), qr) and np.array_equal(host(s), sr)
+    res = gemm.acceptance(bf16_host_f64(y), gemm.scaled_mm_blockwise(qr, sr, b, sb))
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("op,M,N,K", [(BW, 8, 4096, 12288), (MM, 2048, 2048, 6144),
+                                      (BW, 200, 1024, 1024)])
+def test_gemm_deterministic(op, M, N, K):
+    a, sa, b, sb = _gemm_case("det", op, M, N, K, realistic=False)
+    y1 = bf16_host(_run(op, a, sa, b, sb))
+    y2 = bf16_host(_run(op, a, sa, b, sb))
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("cfg,name", [c for c in _configs() if c[1].endswith(("_s1", "_s8"))
+                                      or "_tiled_" in c[1]],
+                         ids=[n for _, n in _configs() if n.endswith(("_s1", "_s8"))
+                              or "_tiled_" in n])
+def test_gemm_writes_stay_in_bounds(cfg, name):
+    M, N, K = _m_for(name), 256, 1024
+    rng = synth.rng_for("canary", name)
+    a = u8_dev(synth.gen_e4m3_codes(rng, (M, K)))
+    b = u8_dev(synth.gen_e4m3_codes(rng, (N, K)))
+    sa, sb = [f32_dev(s) for s in _scales(rng, BW, M, N, K)]
+    buf = torch.full((M * N + 1024,), 3.0, dtype=torch.bfloat16, device=DEV)
+    y = buf[512:512 + M * N].view(M, N)
+    nws = fq.fp8q_workspace_size(BW, M, N, K, cfg)
+    wsbuf = torch.full(((nws // 4) + 128,), -1.0, dtype=torch.float32, device=DEV)
+    ws = wsbuf[64:64 + nws // 4] if nws else None
+    fq.fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws, cfg)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:512] == 3.0) and torch.all(buf[512 + M * N:] == 3.0)
+    assert torch.all(wsbuf[:64] == -1.0) and torch.all(wsbuf[64 + nws // 4:] == -1.0)
+
+
+def test_gemm_m_zero_is_noop():
+    a = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
+    b = torch.zeros((256, 256), dtype=torch.uint8, device=DEV)
+    y = fq.scaled_mm(a, b, torch.empty(0, device=DEV), torch.ones(256, device=DEV))
+    assert y.shape == (0, 256)

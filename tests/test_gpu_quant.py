@@ -1,0 +1,260 @@
+"""GPU parity of the quantizers against the CPU oracle: bytes and scales must
+be bit-identical.  Inputs are the seeded synthetic Qwen3-shaped workloads
+(synth) plus edge cases.
+
+Rounding-tie policy for RMSNorm (the only place two results can be right):
+the GPU sums squares in fp64 in a different order than the oracle's exactly
+rounded sum, so its fp32 inverse RMS may land on the other fp32 neighbour
+when the fp64 value lies within 2^-40 (relative) of an fp32 midpoint.  Such a
+row is accepted only if the oracle, re-run with that other neighbour, then
+matches bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_rms_amd as fq
+import synth
+from oracle import e4m3, quant, silu
+from gpu_util import DEV, bf16_dev, f32_dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+def _rows_sample(M, n=192):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(M)
+    rest = rng.choice(np.arange(1, M - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], rest]))
+
+
+def _check_rms(x, w, mode, rows=None, eps=EPS):
+    M, K = x.shape
+    q, s = fq.rmsnorm_quant(bf16_dev(x), bf16_dev(w), eps, mode)
+    torch.cuda.synchronize()
+    q, s = host(q), host(s)
+    rows = np.arange(M) if rows is None else rows
+    qr, sr = quant.rmsnorm_quant(x[rows], w, eps, mode)
+    qg, sg = q[rows], s[rows]
+    bad = [i for i in range(len(rows))
+           if not (np.array_equal(qg[i], qr[i]) and np.array_equal(sg[i].view(np.uint32),
+                                                                    sr[i].view(np.uint32)))]
+    if bad:
+        inv32, inv64 = quant.rms_inv(x[rows][bad], eps)
+        for j, i in enumerate(bad):
+            lo = np.float32(inv64[j])
+            other = np.nextafter(lo, np.float32(np.inf) if inv64[j] > lo else np.float32(0))
+            mid = (float(lo) + float(other)) / 2
+            assert abs(inv64[j] - mid) <= 2.0 ** -40 * inv64[j], f"row {rows[i]} differs"
+            q2, s2 = quant.rmsnorm_quant(x[rows[i]:rows[i] + 1], w, eps, mode,
+                                         inv_override=np.array([other], np.float32))
+            assert np.array_equal(qg[i], q2[0]) and np.array_equal(sg[i], s2[0]), f"row {rows[i]}"
+    return len(bad)
+
+
+RMS_CASES = [
+    # (name, M, K, mode)
+    ("c1-tiny-group", 16, 256, fq.GROUP128),
+    ("c2-per-token", 1, 2048, fq.PER_TOKEN),
+    ("c2-per-token", 16, 2048, fq.PER_TOKEN),
+    ("c2-per-token", 128, 2048, fq.PER_TOKEN),
+    ("c2-per-token", 2048, 2048, fq.PER_TOKEN),
+    ("c3-group", 1, 4096, fq.GROUP128),
+    ("c3-group", 32, 4096, fq.GROUP128),
+    ("c4-group", 2048, 5120, fq.GROUP128),
+    ("ragged", 37, 5120, fq.PER_TOKEN),
+    ("ragged", 3, 8, fq.PER_TOKEN),
+    ("ragged", 5, 128, fq.GROUP128),
+    ("ragged", 7, 2056, fq.PER_TOKEN),
+    ("max-k", 4, 32768, fq.PER_TOKEN),
+    ("max-k", 4, 32768, fq.GROUP128),
+]
+
+
+@pytest.mark.parametrize("name,M,K,mode", RMS_CASES)
+def test_rmsnorm_quant_parity(name, M, K, mode):
+    say("rmsnorm_quant", name, M, K, mode)
+    rng = synth.rng_for(name, "rmsnorm_quant", M, K)
+    x = synth.gen_activations(rng, M, K)
+    w = synth.gen_rms_weight(rng, K)
+    _check_rms(x, w, mode)
+
+
+@pytest.mark.parametrize("mode", [fq.PER_TOKEN, fq.GROUP128])
+def test_rmsnorm_quant_full_size_sampled(mode):
+    """Qwen3-32B prefill size (M=8192, K=5120), in the bench's launch
+    configuration; 192 sampled rows compared with the oracle."""
+    M, K = 8192, 5120
+    say("rmsnorm_quant sampled", M, K, mode)
+    rng = synth.rng_for("c4-group", "rmsnorm_quant", M, K)
+    x = synth.gen_activations(rng, M, K)
+    w = synth.gen_rms_weight(rng, K)
+    _check_rms(x, w, mode, rows=_rows_sample(M))
+
+
+def test_rmsnorm_quant_edge_rows():
+    K = 256
+    rng = synth.rng_for("edge", "rmsnorm_quant", K)
+    w = synth.gen_rms_weight(rng, K)
+    rows = []
+    rows.append(np.zeros(K, np.float32))                          # all zero
+    z = np.zeros(K, np.float32); z[::3] = -0.0; rows.append(z)     # signed zeros
+    rows.append(np.full(K, 0.75, np.float32))                     # constant
+    rows.append(np.full(K, -3.0e-30, np.float32))                 # tiny scale path
+    t = np.zeros(K, np.float32); t[5] = 1e-35; rows.append(t)     # one tiny element
+    rows.append(np.full(K, 1.0e30, np.float32))                   # huge values
+    h = rng.standard_normal(K).astype(np.float32); h[:128] = 0; rows.append(h)  # zero group
+    o = np.zeros(K, np.float32); o[200] = -5.0; rows.append(o)    # one-hot
+    x = synth.f32_to_bf16_bits(np.stack(rows))
+    for mode in (fq.PER_TOKEN, fq.GROUP128):
+        say("rmsnorm_quant edge", mode)
+        _check_rms(x, w, mode)
+        _check_rms(x, w, mode, eps=1e-30)
+
+
+def _check_silu(gu, mode, rows=None):
+    M, twoD = gu.shape
+    q, s = fq.silu_mul_quant(bf16_dev(gu), mode)
+    torch.cuda.synchronize()
+    q, s = host(q), host(s)
+    rows = np.arange(M) if rows is None else rows
+    qr, sr = quant.silu_mul_quant(gu[rows], mode)
+    assert np.array_equal(q[rows], qr)
+    assert np.array_equal(s[rows].view(np.uint32), sr.view(np.uint32))
+
+
+SILU_CASES = [
+    ("c2-per-token", 1, 6144, fq.PER_TOKEN),
+    ("c2-per-token", 16, 6144, fq.PER_TOKEN),
+    ("c2-per-token", 128, 6144, fq.PER_TOKEN),
+    ("c3-group", 1, 12288, fq.GROUP128),
+    ("c3-group", 32, 12288, fq.GROUP128),
+    ("c5-group", 64, 25600, fq.GROUP128),
+    ("ragged", 9, 1000, fq.PER_TOKEN),
+    ("ragged", 3, 384, fq.GROUP128),
+    ("max-k", 2, 32768, fq.PER_TOKEN),
+]
+
+
+@pytest.mark.parametrize("name,M,D,mode", SILU_CASES)
+def test_silu_mul_quant_parity(name, M, D, mode):
+    say("silu_mul_quant", name, M, D, mode)
+    rng = synth.rng_for(name, "silu_mul_quant", M, D)
+    gu = synth.gen_gate_up(rng, M, D)
+    _check_silu(gu, mode)
+
+
+def test_silu_mul_quant_full_size_sampled():
+    """Qwen3-32B MLP tail at M=4096, D=25600; sampled rows."""
+    M, D = 4096, 25600
+    say("silu_mul_quant sampled", M, D)
+    rng = synth.rng_for("c5-group", "silu_mul_quant", M, D)
+    gu = synth.gen_gate_up(rng, M, D)
+    _check_silu(gu, fq.GROUP128, rows=_rows_sample(M, 96))
+
+
+def test_silu_mul_quant_edge_rows():
+    D = 256
+    g = np.array([0.0, -0.0, 1e-30, -1e-30, 2.0 ** -26, 20.0, 200.0, -200.0, -100.0, -90.0,
+                  1e10, -1e10, 16.5, -16.5, 0.5, -0.5], np.float32)
+    gate = np.resize(g, (4, D)).astype(np.float32)
+    up = np.ones((4, D), np.float32)
+    up[1] = -1.0
+    up[2] = 0.0
+    up[3, ::2] = -0.0
+    gu = synth.f32_to_bf16_bits(np.concatenate([gate, up], axis=1))
+    for mode in (fq.PER_TOKEN, fq.GROUP128):
+        say("silu_mul_quant edge", mode)
+        _check_silu(gu, mode)
+
+
+@pytest.mark.parametrize("mode", [fq.PER_TOKEN, fq.GROUP128])
+def test_standalone_quant_parity(mode):
+    M, K = 64, 4096
+    say("quant", M, K, mode)
+    rng = synth.rng_for("quant", M, K)
+    x = synth.gen_activations(rng, M, K)
+    q, s = fq.quant(bf16_dev(x), mode)
+    torch.cuda.synchronize()
+    qr, sr = quant.quantize(x, mode)
+    assert np.array_equal(host(q), qr)
+    assert np.array_equal(host(s).view(np.uint32), sr.view(np.uint32))
+
+
+def test_silu_exhaustive_all_bf16_gates():
+    """Every one of the 65 536 bf16 gates (NaN patterns excluded) against the
+    oracle's correctly rounded table."""
+    say("silu exhaustive")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    g = bf16_dev(bits)
+    y = torch.empty(65536, dtype=torch.float32, device=DEV)
+    fq.fp8q_silu(y, g)
+    torch.cuda.synchronize()
+    got = host(y).view(np.uint32)
+    want = silu.silu_table().view(np.uint32)
+    exp = (bits.astype(np.uint32) >> 7) & 0xFF
+    man = bits.astype(np.uint32) & 0x7F
+    finite_or_inf = ~((exp == 0xFF) & (man != 0))
+    bad = np.flatnonzero(finite_or_inf & (got != want))
+    assert bad.size == 0, [(hex(int(b)), hex(int(got[b])), hex(int(want[b]))) for b in bad[:8]]
+
+
+def test_e4m3_encoder_exhaustive_range():
+    """The device encoder against the oracle on every fp32 bit pattern from
+    2^-12 to 512 (both signs) and on special values."""
+    lo = int(np.float32(2.0 ** -12).view(np.uint32))
+    hi = int(np.float32(512.0).view(np.uint32))
+    step = 1 << 24
+    for start in range(lo, hi + 1, step):
+        say("e4m3 encoder block", hex(start))
+        bits = np.arange(start, min(start + step, hi + 1), dtype=np.uint32)
+        vals = bits.view(np.float32)
+        for v in (vals, -vals):
+            x = f32_dev(v)
+            q = torch.empty(v.size, dtype=torch.uint8, device=DEV)
+            fq.fp8q_cvt_e4m3(q, x)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(q), e4m3.encode(v)), hex(start)
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-40, -1e-40, 2.0 ** -10, -(2.0 ** -10),
+                        448.0, 448.00003, -448.00003, 460.0, 464.0, 1e6, -1e6, 3.4e38, -3.4e38,
+                        2.0 ** -9, 0.001953125 * 1.5, 0.001953125 * 2.5], np.float32)
+    x = f32_dev(special)
+    q = torch.empty(special.size, dtype=torch.uint8, device=DEV)
+    fq.fp8q_cvt_e4m3(q, x)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), e4m3.encode(special))
+
+
+def test_quant_deterministic_and_no_op():
+    M, K = 64, 5120
+    rng = synth.rng_for("det", M, K)
+    x = bf16_dev(synth.gen_activations(rng, M, K))
+    w = bf16_dev(synth.gen_rms_weight(rng, K))
+    a = fq.rmsnorm_quant(x, w, EPS, fq.PER_TOKEN)
+    b = fq.rmsnorm_quant(x, w, EPS, fq.PER_TOKEN)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # M == 0 is a no-op
+    q, s = fq.rmsnorm_quant(x[:0], w, EPS, fq.GROUP128)
+    assert q.shape == (0, K)
+
+
+def test_quant_writes_stay_in_bounds():
+    """Outputs carved out of larger buffers: the guard bytes around them must
+    be untouched."""
+    M, K = 37, 5120
+    rng = synth.rng_for("canary", M, K)
+    x = bf16_dev(synth.gen_activations(rng, M, K))
+    w = bf16_dev(synth.gen_rms_weight(rng, K))
+    for mode in (fq.PER_TOKEN, fq.GROUP128):
+        ns = M if mode == fq.PER_TOKEN else M * K // 128
+        qbuf = torch.full((M * K + 512,), 0xA5, dtype=torch.uint8, device=DEV)
+        sbuf = torch.full((ns + 128,), -7.0, dtype=torch.float32, device=DEV)
+        q = qbuf[256:256 + M * K].view(M, K)
+        s = sbuf[64:64 + ns]
+        fq.fp8q_rmsnorm_quant(q, s, x, w, EPS, mode)
+        torch.cuda.synchronize()
+        assert torch.all(qbuf[:256] == 0xA5) and torch.all(qbuf[256 + M * K:] == 0xA5)
+        assert torch.all(sbuf[:64] == -7.0) and torch.all(sbuf[64 + ns:] == -7.0)
