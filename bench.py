@@ -1,0 +1,428 @@
+"""Benchmark of the FP8 quantized-linear hot path on one MI355X.
+
+One step = the FP8 linear layers of a Qwen3 decoder layer for every workload
+of the Qwen3 FP8 inference runs (page "Helion in vLLM: FP8 inference of
+Qwen3", 24-ai.news, sections "Kernels integrated into vLLM" and "Whole-model
+speedup"), M from 1 to 8192:
+
+  qwen3-1.7b per-token (hidden 2048)  M in 1,16,128,512,2048:
+      rmsnorm_quant -> scaled_mm qkv; quant(attn out) -> scaled_mm o_proj;
+      rmsnorm_quant -> scaled_mm gate_up; silu_mul_quant -> scaled_mm down
+  qwen3-8b block decode (hidden 4096)  M in 1,2,4,8,16,32:   same chain with
+      1x128 group quantization and scaled_mm_blockwise
+  qwen3-32b block prefill (hidden 5120) M in 2048,8192:       same chain
+  qwen3-32b MLP tail                    M in 64,4096:
+      silu_mul_quant(gate_up [M,51200]) -> scaled_mm_blockwise down
+  tiny blockwise linear                 M = 16: rmsnorm_quant -> 512x256 GEMM
+
+Inputs are seeded synthetic data of the stated distributions (X ~ N(0,1)
+with 1 % outlier columns x20, RMSNorm weight 1+N(0,0.1), gate_up ~ N(0,2),
+weights N(0,0.02) quantized per output channel or per 128x128 block), all
+resident in HBM before timing.  Every (workload, M) has its own weight copy,
+so no GEMM finds its weights in the 256 MB last-level cache from a previous
+launch of the same step.
+
+value = GEMM FLOPs of one step / wall time of one step (quantizer kernels
+included in the time).  The roofline entry is for the dominant kernel (the
+largest share of step time), timed with HIP events on its launch stream
+during the timed steps.  The CPU baseline runs the oracle on a bounded
+sample of that kernel's workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+F16_PEAK_TFLOPS = 2500.0      # MI355X dense f16/bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+PER_TOKEN, GROUP128 = 0, 1
+MM, BW = 0, 1
+
+WORKLOADS = {
+    # name: (mode, hidden, (qkv_n, o_k, gate_up_n, inter), Ms)
+    "qwen3-1.7b-per-token": (PER_TOKEN, 2048, (4096, 2048, 12288, 6144), (1, 16, 128, 512, 2048)),
+    "qwen3-8b-block-decode": (GROUP128, 4096, (6144, 4096, 24576, 12288), (1, 2, 4, 8, 16, 32)),
+    "qwen3-32b-block-prefill": (GROUP128, 5120, (10240, 8192, 51200, 25600), (2048, 8192)),
+}
+MLP_TAIL = ("qwen3-32b-mlp-tail", (64, 4096), 25600, 5120)
+TINY = ("tiny-blockwise", 16, 256, 512)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--detail", default=None, help="write a per-kernel breakdown JSON here")
+    p.add_argument("--cpu-sample-rows", type=int, default=512)
+    return p.parse_args()
+
+
+class Step:
+    """All launches of one step, with pre-allocated buffers and bound C calls."""
+
+    def __init__(self, fq, torch, dev):
+        self.fq, self.torch, self.dev = fq, torch, dev
+        self.lib = fq.lib()
+        self.calls = []     # (label, kind, flops, bytes, callable)
+        self.operands = {}  # GEMM label -> (a, sa, b, sb)
+        self.keep = []      # tensors that must stay alive
+        self.gen = torch.Generator(device=dev)
+        self.gen.manual_seed(20260610)
+        self.ws = None
+        self.ws_bytes = 0
+        self._ws_need = 0
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    # ------------------------------------------------------------ data
+    def randn(self, shape, std=1.0):
+        t = self.torch.randn(shape, generator=self.gen, device=self.dev, dtype=self.torch.float32)
+        return t * std
+
+    def activations(self, M, K):
+        x = self.randn((M, K))
+        n_out = int(round(0.01 * K))
+        cols = self.torch.randperm(K, generator=self.gen, device=self.dev)[:n_out]
+        x[:, cols] *= 20.0
+        return x.to(self.torch.bfloat16).contiguous()
+
+    def weight(self, N, K, mode):
+        """N(0,0.02) fp32 weights quantized with torch ops: per output channel
+        (mode PER_TOKEN) or per 128x128 block (GROUP128).  Input preparation
+        only; not part of the timed path."""
+        torch = self.torch
+        w = self.randn((N, K), 0.02)
+        if mode == PER_TOKEN:
+            s = w.abs().amax(dim=1) / 448.0
+            q = (w / s[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            blk = w.view(N // 128, 128, K // 128, 128)
+            s = blk.abs().amax(dim=(1, 3)) / 448.0
+            q = (blk / s[:, None, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn)
+            q = q.view(torch.uint8).view(N, K)
+        del w
+        return q.contiguous(), s.float().contiguous()
+
+    def empty(self, shape, dtype):
+        t = self.torch.empty(shape, dtype=dtype, device=self.dev)
+        self.keep.append(t)
+        return t
+
+    # --------------------------------------------------------- launches
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: status {rc} "
+                               f"{self.lib.fp8q_status_string(rc).decode()}")
+
+    def add_rmsnorm(self, label, x, w, mode):
+        torch, L = self.torch, self.lib
+        M, K = x.shape
+        q = self.empty((M, K), torch.uint8)
+        s = self.empty((M,) if mode == PER_TOKEN else (M, K // 128), torch.float32)
+        args = (q.data_ptr(), s.data_ptr(), x.data_ptr(), w.data_ptr(), M, K, 1e-6, mode,
+                self.stream)
+        fn = L.fp8q_rmsnorm_quant
+        self.calls.append((label, "rmsnorm_quant", 0, 3 * M * K + 2 * K + s.numel() * 4,
+                           lambda: self._check(fn(*args), label)))
+        self.keep += [x, w]
+        return q, s
+
+    def add_silu(self, label, gu, mode):
+        torch, L = self.torch, self.lib
+        M, twoD = gu.shape
+        D = twoD // 2
+        q = self.empty((M, D), torch.uint8)
+        s = self.empty((M,) if mode == PER_TOKEN else (M, D // 128), torch.float32)
+        args = (q.data_ptr(), s.data_ptr(), gu.data_ptr(), M, D, mode, self.stream)
+        fn = L.fp8q_silu_mul_quant
+        self.calls.append((label, "silu_mul_quant", 0, 5 * M * D + s.numel() * 4,
+                           lambda: self._check(fn(*args), label)))
+        self.keep.append(gu)
+        return q, s
+
+    def add_quant(self, label, x, mode):
+        torch, L = self.torch, self.lib
+        M, K = x.shape
+        q = self.empty((M, K), torch.uint8)
+        s = self.empty((M,) if mode == PER_TOKEN else (M, K // 128), torch.float32)
+        args = (q.data_ptr(), s.data_ptr(), x.data_ptr(), M, K, mode, self.stream)
+        fn = L.fp8q_quant
+        self.calls.append((label, "quant", 0, 3 * M * K + s.numel() * 4,
+                           lambda: self._check(fn(*args), label)))
+        self.keep.append(x)
+        return q, s
+
+    def add_gemm(self, label, op, a, sa, b, sb):
+        torch, L = self.torch, self.lib
+        M, K = a.shape
+        N = b.shape[0]
+        y = self.empty((M, N), torch.bfloat16)
+        need = L.fp8q_workspace_size(op, M, N, K)
+        self._ws_need = max(self._ws_need, need)
+        nbytes = M * K + N * K + 2 * M * N + sa.numel() * 4 + sb.numel() * 4
+        flops = 2 * M * N * K
+        step = self
+
+        if op == MM:
+            fn = L.fp8q_scaled_mm
+
+            def call():
+                step._check(fn(y.data_ptr(), a.data_ptr(), b.data_ptr(), sa.data_ptr(),
+                               sb.data_ptr(), M, N, K, step.ws_ptr, step.ws_bytes, step.stream),
+                            label)
+        else:
+            fn = L.fp8q_scaled_mm_blockwise
+
+            def call():
+                step._check(fn(y.data_ptr(), a.data_ptr(), sa.data_ptr(), b.data_ptr(),
+                               sb.data_ptr(), M, N, K, step.ws_ptr, step.ws_bytes, step.stream),
+                            label)
+        cfg = L.fp8q_gemm_config_for(op, M, N, K)
+        kind = ("scaled_mm" if op == MM else "scaled_mm_blockwise")
+        self.operands[label] = (a, sa, b, sb)
+        self.calls.append((label, kind, flops, nbytes, call))
+        self.keep += [a, sa, b, sb]
+        return y, cfg
+
+    def finalize(self):
+        if self._ws_need:
+            self.ws = self.torch.empty(((self._ws_need + 3) // 4,), dtype=self.torch.float32,
+                                       device=self.dev)
+            self.ws_bytes = self._ws_need
+        self.ws_ptr = self.ws.data_ptr() if self.ws is not None else None
+
+    def run(self, timer=None):
+        for label, kind, flops, nbytes, call in self.calls:
+            if timer is not None and label in timer:
+                ev0 = self.torch.cuda.Event(enable_timing=True)
+                ev1 = self.torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                call()
+                ev1.record()
+                timer[label][0].append(ev0)
+                timer[label][1].append(ev1)
+            else:
+                call()
+
+
+def build(step: Step):
+    torch = step.torch
+    cfg_of = {}
+    for name, (mode, hidden, (qkv_n, o_k, gu_n, inter), Ms) in WORKLOADS.items():
+        op = MM if mode == PER_TOKEN else BW
+        for M in Ms:
+            tag = f"{name}/M{M}"
+            wqkv = step.weight(qkv_n, hidden, mode)
+            wo = step.weight(hidden, o_k, mode)
+            wgu = step.weight(gu_n, hidden, mode)
+            wdn = step.weight(hidden, inter, mode)
+            x = step.activations(M, hidden)
+            rw = (1.0 + step.randn((hidden,), 0.1)).to(torch.bfloat16)
+            q, s = step.add_rmsnorm(f"{tag}/rmsnorm_quant", x, rw, mode)
+            _, c = step.add_gemm(f"{tag}/qkv", op, q, s, *wqkv)
+            cfg_of[f"{tag}/qkv"] = c
+            attn = step.activations(M, o_k)
+            q, s = step.add_quant(f"{tag}/quant_attn", attn, mode)
+            _, c = step.add_gemm(f"{tag}/o_proj", op, q, s, *wo)
+            cfg_of[f"{tag}/o_proj"] = c
+            x2 = step.activations(M, hidden)
+            q, s = step.add_rmsnorm(f"{tag}/rmsnorm_quant2", x2, rw, mode)
+            gu, c = step.add_gemm(f"{tag}/gate_up", op, q, s, *wgu)
+            cfg_of[f"{tag}/gate_up"] = c
+            q, s = step.add_silu(f"{tag}/silu_mul_quant", gu, mode)
+            _, c = step.add_gemm(f"{tag}/down", op, q, s, *wdn)
+            cfg_of[f"{tag}/down"] = c
+    name, Ms, D, hidden = MLP_TAIL
+    for M in Ms:
+        tag = f"{name}/M{M}"
+        wdn = step.weight(hidden, D, GROUP128)
+        gu = (step.randn((M, 2 * D), 2.0)).to(torch.bfloat16)
+        q, s = step.add_silu(f"{tag}/silu_mul_quant", gu, GROUP128)
+        _, c = step.add_gemm(f"{tag}/down", BW, q, s, *wdn)
+        cfg_of[f"{tag}/down"] = c
+    name, M, K, N = TINY
+    tag = f"{name}/M{M}"
+    w = step.weight(N, K, GROUP128)
+    x = step.activations(M, K)
+    rw = (1.0 + step.randn((K,), 0.1)).to(torch.bfloat16)
+    q, s = step.add_rmsnorm(f"{tag}/rmsnorm_quant", x, rw, GROUP128)
+    _, c = step.add_gemm(f"{tag}/linear", BW, q, s, *w)
+    cfg_of[f"{tag}/linear"] = c
+    step.finalize()
+    torch.cuda.synchronize()
+    return cfg_of
+
+
+def per_kernel_times(step: Step, reps: int = 3):
+    """Event-timed duration of every launch (median over reps)."""
+    torch = step.torch
+    times = {label: [] for label, *_ in step.calls}
+    for _ in range(reps):
+        evs = []
+        for label, kind, flops, nbytes, call in step.calls:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            evs.append((label, e0, e1))
+        torch.cuda.synchronize()
+        for label, e0, e1 in evs:
+            times[label].append(e0.elapsed_time(e1) * 1e3)  # us
+    return {k: float(np.median(v)) for k, v in times.items()}
+
+
+def cpu_baseline(step: Step, label: str, rows: int):
+    """The oracle (rmsnorm_quant + blockwise or per-token GEMM as the kernel
+    is) on the first `rows` tokens of the dominant kernel's workload."""
+    import threadpoolctl
+
+    from oracle import gemm as ogemm
+    from oracle import quant as oquant
+
+    entry = next(c for c in step.calls if c[0] == label)
+    a, sa, b, sb = step.operands[label]
+    K = a.shape[1]
+    N = b.shape[0]
+    blockwise = entry[1] == "scaled_mm_blockwise"
+    a_h = a[:rows].cpu().numpy()
+    sa_h = sa[:rows].cpu().numpy()
+    b_h = b.cpu().numpy()
+    sb_h = sb.cpu().numpy()
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    if blockwise:
+        ogemm.scaled_mm_blockwise(a_h, sa_h, b_h, sb_h)
+    else:
+        ogemm.scaled_mm(a_h, b_h, sa_h, sb_h)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{label} ({entry[1]}), first {rows} of {a.shape[0]} tokens, "
+                      f"N={N}, K={K}: fp64 dequantized matmul, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fp8_block_scaled_rms_amd as fq
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    step = Step(fq, torch, dev)
+    cfg_of = build(step)
+    total_flops = sum(c[2] for c in step.calls)
+
+    # warm up, then find the dominant kernel from one event-timed pass
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    kt = per_kernel_times(step)
+    dominant = max(kt, key=kt.get)
+
+    # timed region: K steps, events around the dominant kernel's launches
+    timer = {dominant: ([], [])}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in zip(*timer[dominant])]  # seconds
+    dom_avg = float(np.mean(durs))
+    dom = next(c for c in step.calls if c[0] == dominant)
+    dom_cfg = cfg_of.get(dominant)
+    dom_cfg_name = fq.fp8q_gemm_config_name(dom_cfg) if dom_cfg is not None else None
+    exact = dom_cfg_name is None or dom_cfg_name.startswith("f16_")
+    if dom[2] > 0:
+        achieved = dom[2] / dom_avg / 1e12
+        peak = F16_PEAK_TFLOPS if exact else FP8_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": dominant, "variant": dom_cfg_name,
+                "avg_launch_us": round(dom_avg * 1e6, 2),
+                "frac_of_fp8_peak": round(achieved / FP8_PEAK_TFLOPS, 4)}
+    else:
+        achieved = dom[3] / dom_avg / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dominant, "avg_launch_us": round(dom_avg * 1e6, 2)}
+
+    # per-workload summary from the event-timed pass
+    summary = {}
+    for label, kind, flops, nbytes, _ in step.calls:
+        wl = label.split("/")[0]
+        s = summary.setdefault(wl, {"gemm_us": 0.0, "quant_us": 0.0, "gemm_flops": 0.0})
+        if flops:
+            s["gemm_us"] += kt[label]
+            s["gemm_flops"] += flops
+        else:
+            s["quant_us"] += kt[label]
+    per_wl = {wl: {"gemm_tflops": round(s["gemm_flops"] / (s["gemm_us"] * 1e-6) / 1e12, 1),
+                   "gemm_us": round(s["gemm_us"], 1), "quant_us": round(s["quant_us"], 1)}
+              for wl, s in summary.items()}
+
+    cpu = None
+    if not args.no_cpu_baseline and dom[2] > 0:
+        cpu = cpu_baseline(step, dominant, args.cpu_sample_rows)
+
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s & % FP8 MFMA peak, Qwen3 shapes M=1..8192",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-fp8-linear-sweep",
+                   "parts": list(WORKLOADS) + [MLP_TAIL[0], TINY[0]],
+                   "gemm_flops_per_step": total_flops,
+                   "launches_per_step": len(step.calls),
+                   "parallelism": "single-gpu"},
+        "frac_of_fp8_peak": round(value / FP8_PEAK_TFLOPS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_workload": per_wl,
+    }
+    if args.detail:
+        detail = {label: {"kind": kind, "us": round(kt[label], 2), "flops": flops,
+                          "bytes": nbytes,
+                          "variant": (fq.fp8q_gemm_config_name(cfg_of[label])
+                                      if label in cfg_of else None)}
+                  for label, kind, flops, nbytes, _ in step.calls}
+        with open(args.detail, "w") as f:
+            json.dump(detail, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
