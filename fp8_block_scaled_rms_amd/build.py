@@ -34,6 +34,9 @@ HIPCC_FLAGS = [
     "-fno-fast-math",
     # no packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the blockwise scale FMA reads them
+    # directly instead of copying each one out of the accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", INCLUDE, "-I", CSRC, "-I", BUILD,
 ]

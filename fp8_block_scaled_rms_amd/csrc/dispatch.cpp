@@ -59,7 +59,7 @@ int rule(int op, long M, long N, long K) {
     int id = find_skinny(tm, rw, wk, split);
     if (id >= 0) return id;
   }
-  if (N % 128 == 0) return find_variant("f16_tiled_m128_n128_w2x2");
+  if (N % 128 == 0) return find_variant("f16_tiled_m128_n128_w2x2_st2");
   return -1;
 }
 

@@ -122,13 +122,26 @@ __device__ __forceinline__ v4f block_mma(const Frag<E>& w, const Frag<E>& x, v4f
   }
 }
 
-// Direct global -> LDS loads.  `lds` must be wave-uniform: lane i's data
-// lands at lds + i * size.
-__device__ __forceinline__ void g2lds16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds, 16, 0, 0);
+// Direct global -> LDS loads (global_load_lds_dword[x4]): the data of lane i
+// lands at lds + i * size, `lds` being a wave-uniform LDS byte address (it is
+// passed in M0).  They are issued from inline assembly on purpose: the
+// compiler cannot tell which LDS buffer such a load writes, so for the
+// intrinsic it drains every load in flight before each LDS read, which would
+// serialise the multi-stage pipeline.  Completion is instead tracked
+// explicitly with s_waitcnt vmcnt (wait_stage) followed by a workgroup
+// barrier before the stage is read.  The instructions write no registers.
+// M0 is not allocated by the compiler in these kernels (it reserves it), so
+// setting it here disturbs nothing.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)p));
 }
-__device__ __forceinline__ void g2lds4(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds, 4, 0, 0);
+__device__ __forceinline__ void g2lds16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+               : "memory");
+}
+__device__ __forceinline__ void g2lds4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
+               : "memory");
 }
 
 // 16-byte-chunk swizzle of a 128-byte LDS row: rows 0..7 use distinct chunks
@@ -155,7 +168,6 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   return f;
 }
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* y, float a, float b, float c, float d) {
   uint2 v;
@@ -165,27 +177,76 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* y, float a, float b, floa
 }
 
 // ------------------------------------------------------------- tiled --
-template <int BM, int BN, int WM, int WN, bool BLOCK>
+// Workgroup -> output tile.  Workgroups are dispatched round-robin over the
+// 8 XCDs (workgroup b runs on XCD b % 8) and each XCD has its own L2, so
+// first every XCD is given one contiguous range of logical tile ids; inside
+// that range tiles are walked in groups of kGroupRows token-tile rows, column
+// by column, so the workgroups resident at the same time share a few token
+// tiles and a few weight tiles instead of streaming whole operands.
+constexpr int kXcds = 8;
+constexpr int kGroupRows = 8;
+
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tn, int& tm) {
+  const int ntiles = tiles_m * tiles_n;
+  const int q = ntiles / kXcds, r = ntiles % kXcds;
+  const int xcd = b % kXcds, local = b / kXcds;
+  const int logical = xcd * q + (xcd < r ? xcd : r) + local;
+  const int group_tiles = kGroupRows * tiles_n;
+  const int group = logical / group_tiles;
+  const int first_m = group * kGroupRows;
+  const int rows = (tiles_m - first_m < kGroupRows) ? tiles_m - first_m : kGroupRows;
+  const int in_group = logical - group * group_tiles;
+  tm = first_m + in_group % rows;
+  tn = in_group / rows;
+}
+
+template <int BM, int BN, int WM, int WN, int ST, bool BLOCK>
 struct TiledShape {
   static constexpr int kThreads = WM * WN * 64;
+  static constexpr int kWaves = WM * WN;
   static constexpr int kTM = BM / WM;   // tokens per wave
   static constexpr int kTN = BN / WN;   // weight rows per wave
   static constexpr int kFT = kTM / 16;  // token fragments per wave
   static constexpr int kFW = kTN / 16;  // weight fragments per wave
   static constexpr int kXBytes = BM * kBK;
   static constexpr int kWBytes = BN * kBK;
-  static constexpr int kStage = kXBytes + kWBytes + (BLOCK ? BM * 4 : 0);
-  static constexpr int kLds = 2 * kStage;
+  // blockwise: one 64-float segment per wave holding [sa column | sb row | pad]
+  static constexpr int kSBytes = BLOCK ? kWaves * 256 : 0;
+  static constexpr int kStage = kXBytes + kWBytes + kSBytes;
+  static constexpr int kLds = ST * kStage;
+  // global->LDS load instructions each wave issues per stage (all equal)
+  static constexpr int kLoadsPerStage = (BM * 8 + BN * 8) / kThreads + (BLOCK ? 1 : 0);
   static_assert((BM * 8) % kThreads == 0 && (BN * 8) % kThreads == 0, "tile/threads");
   static_assert(128 % kTN == 0, "a wave's weight rows must sit in one 128-row block");
-  static_assert(BM % 64 == 0, "token tile in whole waves for the scale load");
+  static_assert(!BLOCK || BM + 64 <= 64 * kWaves, "scale segments");
+  static_assert(ST >= 2 && kLoadsPerStage * (ST - 2) < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int WM, int WN, bool BLOCK, int E>
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int L, int ST>
+__device__ __forceinline__ void wait_stage(int after) {
+  // `after` = stages issued after the one needed, 0 <= after <= ST - 2
+  if constexpr (ST >= 4) {
+    if (after >= 2) { wait_vm<L * (ST - 2)>(); return; }
+  }
+  if constexpr (ST >= 3) {
+    if (after >= 1) { wait_vm<L>(); return; }
+  }
+  wait_vm<0>();
+}
+
+// ST-stage ring of LDS buffers fed by direct global->LDS loads: the loads of
+// K block kb+ST-1 are in flight while block kb is multiplied, which covers
+// the HBM/L2 latency at the consumption rate of the matrix cores.
+template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     uint16_t* __restrict__ y, const uint8_t* __restrict__ A, const float* __restrict__ sa,
     const uint8_t* __restrict__ B, const float* __restrict__ sb, int M, int N, int K) {
-  using S = TiledShape<BM, BN, WM, WN, BLOCK>;
+  using S = TiledShape<BM, BN, WM, WN, ST, BLOCK>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -194,35 +255,55 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   const int wn = wave % WN, wm = wave / WN;
   const int lr = lane & 15, g = lane >> 4;
 
-  const int tiles_n = N / BN;
-  const int tn = blockIdx.x % tiles_n, tmi = blockIdx.x / tiles_n;
+  int tn, tmi;
+  tile_coords(blockIdx.x, (M + BM - 1) / BM, N / BN, tn, tmi);
   const int n0 = tn * BN, m0 = tmi * BM;
   const int KB = K / kBK;
 
+  // per-thread, K-block-invariant parts of the load addresses
+  uint32_t a_off[BM * 8 / S::kThreads], b_off[BN * 8 / S::kThreads];
+#pragma unroll
+  for (int j = 0; j < BM * 8 / S::kThreads; ++j) {
+    const int qi = j * S::kThreads + tid;
+    const int r = qi >> 3, p = qi & 7;
+    const int row = (m0 + r < M) ? m0 + r : M - 1;
+    a_off[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < BN * 8 / S::kThreads; ++j) {
+    const int qi = j * S::kThreads + tid;
+    const int r = qi >> 3, p = qi & 7;
+    b_off[j] = static_cast<uint32_t>(n0 + r) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
+  }
+  // blockwise scales: wave w fetches floats [64w, 64w+64) of [sa column | sb | pad]
+  const float* s_src = sa;
+  long s_off = 0;
+  if constexpr (BLOCK) {
+    const int q = wave * 64 + lane;
+    if (q < BM) {
+      const int row = (m0 + q < M) ? m0 + q : M - 1;
+      s_off = static_cast<long>(row) * KB;
+    } else if (q < BM + BN / 128) {
+      s_src = sb;
+      s_off = static_cast<long>(n0 / 128 + (q - BM)) * KB;
+    } else {
+      s_off = static_cast<long>(m0) * KB;  // padding: any valid address
+    }
+  }
+
+  const uint32_t lds0 = lds_address(smem);
   auto load_stage = [&](int kb, int buf) {
-    uint8_t* base = smem + buf * S::kStage;
+    const uint32_t base = lds0 + buf * S::kStage + wave * 64 * 16;
+    const uint8_t* Ak = A + static_cast<long>(kb) * kBK;
+    const uint8_t* Bk = B + static_cast<long>(kb) * kBK;
 #pragma unroll
-    for (int j = 0; j < BM * 8 / S::kThreads; ++j) {
-      const int qi = j * S::kThreads + tid;
-      const int r = qi >> 3, p = qi & 7;
-      const int row = (m0 + r < M) ? m0 + r : M - 1;
-      g2lds16(A + static_cast<long>(row) * K + kb * kBK + ((p ^ swz(r)) << 4),
-              base + (j * S::kThreads + wave * 64) * 16);
-    }
+    for (int j = 0; j < BM * 8 / S::kThreads; ++j)
+      g2lds16(Ak + a_off[j], base + j * S::kThreads * 16);
 #pragma unroll
-    for (int j = 0; j < BN * 8 / S::kThreads; ++j) {
-      const int qi = j * S::kThreads + tid;
-      const int r = qi >> 3, p = qi & 7;
-      g2lds16(B + static_cast<long>(n0 + r) * K + kb * kBK + ((p ^ swz(r)) << 4),
-              base + S::kXBytes + (j * S::kThreads + wave * 64) * 16);
-    }
-    if constexpr (BLOCK) {
-      for (int j = wave; j < BM / 64; j += S::kThreads / 64) {
-        const int r = j * 64 + lane;
-        const int row = (m0 + r < M) ? m0 + r : M - 1;
-        g2lds4(sa + static_cast<long>(row) * KB + kb, base + S::kXBytes + S::kWBytes + j * 256);
-      }
-    }
+    for (int j = 0; j < BN * 8 / S::kThreads; ++j)
+      g2lds16(Bk + b_off[j], base + S::kXBytes + j * S::kThreads * 16);
+    if constexpr (BLOCK)
+      g2lds4(s_src + s_off + kb, lds0 + buf * S::kStage + S::kXBytes + S::kWBytes + wave * 256);
   };
 
   v4f acc[S::kFW][S::kFT];
@@ -231,11 +312,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
     for (int t = 0; t < S::kFT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0, 0);
+#pragma unroll
+  for (int p = 0; p < ST - 1; ++p)
+    if (p < KB) load_stage(p, p);
+
   for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    wait_vm_all();
-    __syncthreads();
+    const int buf = kb % ST;
+    const int after = (KB - 1 - kb < ST - 2) ? KB - 1 - kb : ST - 2;
+    wait_stage<S::kLoadsPerStage, ST>(after);
+    // Block kb is in LDS (each wave waited for its own loads, whose data is
+    // written before the counter drops) and every wave is done reading kb-1.
+    // A bare s_barrier: __syncthreads() would also wait for the loads of the
+    // later stages still in flight.
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     const uint8_t* xs = smem + buf * S::kStage;
     const uint8_t* ws = xs + S::kXBytes;
     v8i xr[S::kFT], wr[S::kFW];
@@ -246,11 +336,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     float sab[S::kFT];
     if constexpr (BLOCK) {
       const float* sas = reinterpret_cast<const float*>(ws + S::kWBytes);
-      const float sw = sb[static_cast<long>((n0 + wn * S::kTN) / 128) * KB + kb];
+      const float sw = sas[BM + (wn * S::kTN) / 128];
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) sab[t] = sas[wm * S::kTM + 16 * t + lr] * sw;
     }
-    if (kb + 1 < KB) load_stage(kb + 1, buf ^ 1);
+    // the buffer of block kb-1 is free: refill it with block kb+ST-1
+    if (kb + ST - 1 < KB) load_stage(kb + ST - 1, (kb + ST - 1) % ST);
     Frag<E> xf[S::kFT];
 #pragma unroll
     for (int t = 0; t < S::kFT; ++t) xf[t] = prep<E>(xr[t]);
@@ -467,17 +558,18 @@ const char* keep_name(const std::string& n) {
   return names.back()->c_str();
 }
 
-template <int BM, int BN, int WM, int WN, int E>
+template <int BM, int BN, int WM, int WN, int ST, int E>
 Variant tiled_variant() {
   Variant v{};
   const char* name = keep_name(std::string(E == kEngineF8 ? "f8" : "f16") + "_tiled_m" +
                                std::to_string(BM) + "_n" + std::to_string(BN) + "_w" +
-                               std::to_string(WM) + "x" + std::to_string(WN));
+                               std::to_string(WM) + "x" + std::to_string(WN) + "_st" +
+                               std::to_string(ST));
   v.cfg = GemmConfig{name, kTiled, E, BM, BN, WM, WN, 0, 0, 0, 1};
-  v.fn[0] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, false, E>);
-  v.fn[1] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, true, E>);
+  v.fn[0] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, false, E>);
+  v.fn[1] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E>);
   v.threads = WM * WN * 64;
-  v.lds = TiledShape<BM, BN, WM, WN, true>::kLds;  // the larger of the two
+  v.lds = TiledShape<BM, BN, WM, WN, ST, true>::kLds;  // the larger of the two
   return v;
 }
 
@@ -498,14 +590,16 @@ Variant skinny_variant(int split) {
 std::vector<Variant>& registry() {
   static std::vector<Variant> r = [] {
     std::vector<Variant> v;
-    v.push_back(tiled_variant<128, 128, 2, 2, kEngineF16>());
-    v.push_back(tiled_variant<256, 128, 2, 2, kEngineF16>());
-    v.push_back(tiled_variant<128, 256, 2, 4, kEngineF16>());
-    v.push_back(tiled_variant<64, 128, 1, 2, kEngineF16>());
-    v.push_back(tiled_variant<128, 128, 2, 2, kEngineF8>());
-    v.push_back(tiled_variant<256, 128, 2, 2, kEngineF8>());
-    v.push_back(tiled_variant<128, 256, 2, 4, kEngineF8>());
-    v.push_back(tiled_variant<64, 128, 1, 2, kEngineF8>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 3, kEngineF16>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineF16>());
+    v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF16>());
+    v.push_back(tiled_variant<256, 128, 4, 2, 3, kEngineF16>());
+    v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF8>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineF8>());
+    v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF8>());
+    v.push_back(tiled_variant<256, 128, 4, 2, 3, kEngineF8>());
 #define FP8Q_SKINNY(T, R, W) \
   for (int s : {1, 2, 4, 8}) v.push_back(skinny_variant<T, R, W, kEngineF16>(s));
     FP8Q_SKINNY(1, 1, 4)

@@ -1,0 +1,181 @@
+"""Measure every applicable GEMM variant per shape on the GPU and write the
+per-shape dispatch table (csrc/tune_table.inc).
+
+The table is how the library picks, per (op, N, K, M), between the tiled
+kernel, the weight-streaming small-M kernel and their split-K / tile-shape
+parameters (page "Helion can accelerate vLLM LLM inference on NVIDIA GPUs",
+aihirek.info, section "Autotuning picks the right variant": the algorithm is
+a tuned parameter chosen per shape instead of a hand-written rule).
+
+    python -m fp8_block_scaled_rms_amd.tune --out results.jsonl [--write-table]
+        [--engine exact|fp8|all] [--shapes default|quick]
+
+Results are appended to a JSONL file, one line per (shape, variant), and a
+rerun skips what the file already holds (resumable).  Timing: HIP events
+around each launch on the current stream, median of the repetitions; every
+repetition reads its own copy of the weights, rotating through >= 1 GiB of
+copies, so no run is served by the 256 MB last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import fp8_block_scaled_rms_amd as fq  # noqa: E402
+
+MM, BW = fq.OP_SCALED_MM, fq.OP_SCALED_MM_BLOCKWISE
+
+# every GEMM of the Qwen3 FP8 workloads
+SHAPES = (
+    [(MM, M, N, K) for M in (1, 16, 128, 512, 2048)
+     for N, K in ((4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144))]
+    + [(BW, M, N, K) for M in (1, 2, 4, 8, 16, 32)
+       for N, K in ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288))]
+    + [(BW, M, N, K) for M in (2048, 8192)
+       for N, K in ((10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600))]
+    + [(BW, 64, 5120, 25600), (BW, 4096, 5120, 25600), (BW, 16, 512, 256)]
+)
+# M buckets between measured M values are served by the next larger one
+QUICK = [(BW, 8192, 51200, 5120), (BW, 2048, 10240, 5120), (BW, 32, 24576, 4096),
+         (BW, 1, 4096, 4096), (MM, 2048, 12288, 2048), (MM, 128, 12288, 2048)]
+
+
+def variants(op, M, N, K, engine):
+    out = []
+    for i in range(fq.fp8q_gemm_num_configs()):
+        name = fq.fp8q_gemm_config_name(i)
+        if engine == "exact" and not name.startswith("f16_"):
+            continue
+        if engine == "fp8" and not name.startswith("f8_"):
+            continue
+        if "_skinny_" in name:
+            tm = int(name.split("_skinny_t")[1].split("_")[0])
+            if M > 16 * tm or (tm > 1 and M <= 8 * tm):  # too small a fit is pointless
+                continue
+            rw = int(name.split("_r")[1].split("_")[0])
+            if N % (16 * rw):
+                continue
+        else:
+            if M <= 16:
+                continue
+            bn = int(name.split("_n")[1].split("_")[0])
+            if N % bn:
+                continue
+        out.append((i, name))
+    return out
+
+
+def time_shape(op, M, N, K, cands, reps=10):
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(M * 7919 + N * 31 + K)
+    wbytes = N * K
+    copies = max(1, min(reps, (1 << 30) // max(wbytes, 1) + 1))
+    a = torch.randint(0, 255, (M, K), generator=g, device=dev, dtype=torch.uint8) & 0xF7
+    bs = [torch.randint(0, 255, (N, K), generator=g, device=dev, dtype=torch.uint8) & 0xF7
+          for _ in range(copies)]
+    if op == MM:
+        sa = torch.rand(M, generator=g, device=dev) + 0.5
+        sb = torch.rand(N, generator=g, device=dev) + 0.5
+    else:
+        sa = torch.rand(M, K // 128, generator=g, device=dev) + 0.5
+        sb = torch.rand(N // 128, K // 128, generator=g, device=dev) + 0.5
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    res = {}
+    for cfg, name in cands:
+        nws = fq.fp8q_workspace_size(op, M, N, K, cfg)
+        ws = torch.empty((nws + 3) // 4, dtype=torch.float32, device=dev) if nws else None
+
+        def run(b):
+            if op == MM:
+                fq.fp8q_scaled_mm(y, a, b, sa, sb, ws, cfg)
+            else:
+                fq.fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws, cfg)
+
+        for w in range(2):
+            run(bs[w % copies])
+        evs = []
+        for r in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run(bs[r % copies])
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        res[name] = ts[len(ts) // 2]
+    return res
+
+
+def write_table(rows, path):
+    """rows: list of (op, M, N, K, best_name).  One table row per measured M;
+    the row's M_max is that M, the largest measured M of a family also
+    serves everything above it."""
+    fam = {}
+    for op, M, N, K, name in rows:
+        fam.setdefault((op, N, K), []).append((M, name))
+    lines = ["// Per-shape GEMM variant table: {op, N, K, M_max, variant name}.",
+             "// op 0 = scaled_mm, 1 = scaled_mm_blockwise.  For a call (op, M, N, K) the",
+             "// first row with the same op, N and K and M <= M_max wins; shapes absent",
+             "// from the table use the built-in rule in dispatch.cpp.",
+             "// Written by fp8_block_scaled_rms_amd/tune.py from MI355X measurements."]
+    for (op, N, K), ms in sorted(fam.items()):
+        ms.sort()
+        for j, (M, name) in enumerate(ms):
+            m_max = M if j + 1 < len(ms) else 1 << 30
+            lines.append(f'{{{op}, {N}, {K}, {m_max}, "{name}"}},')
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default="tune_results.jsonl")
+    ap.add_argument("--engine", default="exact", choices=["exact", "fp8", "all"])
+    ap.add_argument("--shapes", default="default", choices=["default", "quick"])
+    ap.add_argument("--write-table", default=None, help="path of the table to write")
+    ap.add_argument("--reps", type=int, default=10)
+    args = ap.parse_args()
+    done = {}
+    if os.path.exists(args.out):
+        with open(args.out) as f:
+            for line in f:
+                r = json.loads(line)
+                done[(r["op"], r["M"], r["N"], r["K"], r["variant"])] = r["us"]
+    shapes = SHAPES if args.shapes == "default" else QUICK
+    best_rows = []
+    with open(args.out, "a") as f:
+        for op, M, N, K in shapes:
+            cands = variants(op, M, N, K, args.engine)
+            todo = [(c, n) for c, n in cands if (op, M, N, K, n) not in done]
+            if todo:
+                res = time_shape(op, M, N, K, todo, args.reps)
+                for n, us in res.items():
+                    done[(op, M, N, K, n)] = us
+                    f.write(json.dumps({"op": op, "M": M, "N": N, "K": K, "variant": n,
+                                        "us": round(us, 3)}) + "\n")
+                f.flush()
+            mine = {n: done[(op, M, N, K, n)] for _, n in cands}
+            best = min(mine, key=mine.get)
+            flops = 2.0 * M * N * K
+            byts = M * K + N * K + 2 * M * N
+            print(f"op{op} M={M:5d} N={N:6d} K={K:6d} best {best:30s} {mine[best]:9.1f}us "
+                  f"{flops / mine[best] / 1e6:8.1f}TF {byts / mine[best] / 1e3:7.0f}GB/s "
+                  f"({len(mine)} variants)", flush=True)
+            best_rows.append((op, M, N, K, best))
+    if args.write_table:
+        write_table(best_rows, args.write_table)
+
+
+if __name__ == "__main__":
+    main()
