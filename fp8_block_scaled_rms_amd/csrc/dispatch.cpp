@@ -33,30 +33,27 @@ int find_variant(const char* name) {
   return -1;
 }
 
-int find_skinny(int tm, int rw, int wk, int split) {
+int find_skinny(int tm, int rw, int wk, int j) {
   const int n = gemm_num_configs();
   for (int i = 0; i < n; ++i) {
     const GemmConfig& c = gemm_config(i);
     if (c.kind == kSkinny && c.engine == kEngineExact && c.tm == tm && c.rw == rw &&
-        c.wk == wk && c.split == split)
+        c.wk == wk && c.split == j)
       return i;
   }
   return -1;
 }
 
-// Fixed rule for shapes without a measured row (exact engine only).
+// Fixed rule for shapes without a measured row (exact engine only): the
+// weight-streaming kernel up to 128 tokens, the tiled kernel above.
 int rule(int op, long M, long N, long K) {
   (void)op;
+  (void)K;
   if (M <= 128) {
     const int tm = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-    const int rw = (N % 32 == 0) ? 2 : 1;
-    const int wk = tm == 8 ? 4 : 8;
-    const long kb = K / 128;
-    int split = 1;
-    // enough workgroups to cover the chip twice, while every wave keeps
-    // at least two K blocks
-    while ((N / (16 * rw)) * split < 512 && split < 8 && kb / (2L * split) >= 2L * wk) split *= 2;
-    int id = find_skinny(tm, rw, wk, split);
+    const int rw = (N >= 8192 && N % 32 == 0) ? 2 : 1;
+    const int j = tm <= 2 ? 8 : tm == 4 ? 4 : 2;
+    const int id = find_skinny(tm, rw, 4, j);
     if (id >= 0) return id;
   }
   if (N % 128 == 0) return find_variant("f16_tiled_m128_n128_w2x2_st2");

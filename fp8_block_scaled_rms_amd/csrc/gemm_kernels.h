@@ -12,9 +12,10 @@ namespace fp8q {
 //                 tokens, wn x wm waves; every operand byte is read from HBM
 //                 once per tile row/column.
 //   kind kSkinny: weight-streaming kernel for small M: a workgroup owns
-//                 rw*16 weight rows and all (<= tm*16) tokens, its wk waves
-//                 split K and are reduced through LDS; `split` > 1 also splits
-//                 K across workgroups through an fp32 workspace.
+//                 rw*16 weight rows and all (<= tm*16) tokens; each of its wk
+//                 waves loads `split` (= j) K blocks at once; the waves are
+//                 reduced through LDS, and K longer than wk*j blocks is split
+//                 across workgroups through an fp32 workspace.
 // Both keep the weight rows on the 16-row side of the 16x16x128 MFMA and the
 // tokens on the 16-column side (the swap-AB orientation).
 enum GemmKind { kTiled = 0, kSkinny = 1 };
@@ -29,7 +30,7 @@ struct GemmConfig {
   int engine;
   int bm, bn, wm, wn;  // kTiled
   int tm, rw, wk;      // kSkinny
-  int split;           // kSkinny: workgroups along K (1 = none)
+  int split;           // kSkinny: K blocks per wave (j)
 };
 
 int gemm_num_configs();

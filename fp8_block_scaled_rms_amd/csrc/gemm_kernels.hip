@@ -182,7 +182,10 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* y, float a, float b, floa
 // first every XCD is given one contiguous range of logical tile ids; inside
 // that range tiles are walked in groups of kGroupRows token-tile rows, column
 // by column, so the workgroups resident at the same time share a few token
-// tiles and a few weight tiles instead of streaming whole operands.
+// tiles and a few weight tiles in L2 instead of streaming whole operands.
+// (Cutting the tile grid into per-XCD rectangles that minimise the operand
+// bytes each XCD fetches measured no faster on the Qwen3 shapes: the 256 MB
+// last-level cache serves the repeated weight reads.)
 constexpr int kXcds = 8;
 constexpr int kGroupRows = 8;
 
@@ -385,7 +388,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 }
 
 // ------------------------------------------------------------ skinny --
-template <int TMX, int RW, int WK, bool BLOCK, int E>
+// Small M: the weight matrix is the HBM traffic, so the kernel is built to
+// keep enough bytes in flight.  A workgroup owns RW*16 weight rows and all
+// tokens (<= TMX*16); each of its WK waves owns J K blocks (interleaved
+// across the waves) and issues the loads of all of them before the first
+// MFMA.  The WK partial sums are added through LDS in wave order; when K
+// needs more than WK*J blocks, further workgroups along K write fp32
+// partials that splitk_reduce_kernel adds in order.
+template <int TMX, int RW, int WK, int J, bool BLOCK, int E>
 __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
     uint16_t* __restrict__ y, float* __restrict__ ws, const uint8_t* __restrict__ A,
     const float* __restrict__ sa, const uint8_t* __restrict__ B, const float* __restrict__ sb,
@@ -397,9 +407,7 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
   const int n0 = blockIdx.x * RW * 16;
   const int s = blockIdx.y;
   const int KB = K / kBK;
-  const int per = (KB + SPLIT - 1) / SPLIT;
-  const int kb_lo = s * per;
-  const int kb_hi = (kb_lo + per < KB) ? kb_lo + per : KB;
+  const int kb0 = s * (WK * J) + wave;  // this wave: kb0, kb0 + WK, ...
 
   const uint8_t* wrow[RW];
 #pragma unroll
@@ -414,86 +422,67 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
   }
   const long sb_row = static_cast<long>(n0 / 128) * KB;
 
+  // issue every load of this wave first
+  v8i wr[J][RW], xr[J][TMX];
+  float sab[J][TMX];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int kb = kb0 + WK * j;
+    const bool on = kb < KB;
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      wr[j][i] = on ? load_frag_global(wrow[i] + kb * kBK) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < TMX; ++t)
+      xr[j][t] = (on && xok[t]) ? load_frag_global(xrow[t] + kb * kBK)
+                                : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (BLOCK) {
+      const float sw = on ? sb[sb_row + kb] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < TMX; ++t)
+        sab[j][t] = (on && xok[t]) ? sa[static_cast<long>(16 * t + lr) * KB + kb] * sw : 0.0f;
+    }
+  }
+
   v4f acc[RW][TMX];
 #pragma unroll
   for (int i = 0; i < RW; ++i)
 #pragma unroll
     for (int t = 0; t < TMX; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  auto step = [&](const v8i* wr, const v8i* xr, const float* sab) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (kb0 + WK * j >= KB) break;
     Frag<E> xf[TMX];
 #pragma unroll
-    for (int t = 0; t < TMX; ++t) xf[t] = prep<E>(xr[t]);
+    for (int t = 0; t < TMX; ++t) xf[t] = prep<E>(xr[j][t]);
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const Frag<E> wf = prep<E>(wr[i]);
+      const Frag<E> wf = prep<E>(wr[j][i]);
 #pragma unroll
       for (int t = 0; t < TMX; ++t) {
         if constexpr (BLOCK) {
           const v4f p = block_mma<E>(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[j][t], acc[i][t][r]);
         } else {
           acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
         }
       }
     }
-  };
-  auto load = [&](int kb, v8i* wf, v8i* xf, float* sab) {
-#pragma unroll
-    for (int i = 0; i < RW; ++i) wf[i] = load_frag_global(wrow[i] + kb * kBK);
-#pragma unroll
-    for (int t = 0; t < TMX; ++t) {
-      if (xok[t]) {
-        xf[t] = load_frag_global(xrow[t] + kb * kBK);
-      } else {
-        xf[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-    if constexpr (BLOCK) {
-      const float sw = sb[sb_row + kb];
-#pragma unroll
-      for (int t = 0; t < TMX; ++t)
-        sab[t] = xok[t] ? sa[static_cast<long>(16 * t + lr) * KB + kb] * sw : 0.0f;
-    }
-  };
-
-  int kb = kb_lo + wave;
-  for (; kb + WK < kb_hi; kb += 2 * WK) {
-    v8i wf0[RW], xf0[TMX], wf1[RW], xf1[TMX];
-    float sab0[TMX], sab1[TMX];
-    load(kb, wf0, xf0, sab0);
-    load(kb + WK, wf1, xf1, sab1);
-    step(wf0, xf0, sab0);
-    step(wf1, xf1, sab1);
-  }
-  if (kb < kb_hi) {
-    v8i wf0[RW], xf0[TMX];
-    float sab0[TMX];
-    load(kb, wf0, xf0, sab0);
-    step(wf0, xf0, sab0);
   }
 
-  // reduce the WK waves' partial sums in a fixed order
+  // add the WK waves' partial sums in a fixed order
   constexpr int kFrags = RW * TMX;
-  if constexpr (WK > 1) {
-    v4f* r4 = reinterpret_cast<v4f*>(red);
+  v4f* r4 = reinterpret_cast<v4f*>(red);
 #pragma unroll
-    for (int i = 0; i < RW; ++i)
+  for (int i = 0; i < RW; ++i)
 #pragma unroll
-      for (int t = 0; t < TMX; ++t) r4[(wave * kFrags + i * TMX + t) * 64 + lane] = acc[i][t];
-    __syncthreads();
-  }
-  for (int f = (WK > 1 ? wave : 0); f < kFrags; f += WK) {
+    for (int t = 0; t < TMX; ++t) r4[(wave * kFrags + i * TMX + t) * 64 + lane] = acc[i][t];
+  __syncthreads();
+  for (int f = wave; f < kFrags; f += WK) {
     const int i = f / TMX, t = f % TMX;
-    v4f v;
-    if constexpr (WK > 1) {
-      const v4f* r4 = reinterpret_cast<const v4f*>(red);
-      v = r4[f * 64 + lane];
-      for (int w = 1; w < WK; ++w) v += r4[(w * kFrags + f) * 64 + lane];
-    } else {
-      v = acc[i][t];
-    }
+    v4f v = r4[f * 64 + lane];
+    for (int w = 1; w < WK; ++w) v += r4[(w * kFrags + f) * 64 + lane];
     const int m = 16 * t + lr;
     if (m >= M) continue;
     const int n = n0 + 16 * i + 4 * g;
@@ -573,17 +562,17 @@ Variant tiled_variant() {
   return v;
 }
 
-template <int TMX, int RW, int WK, int E>
-Variant skinny_variant(int split) {
+template <int TMX, int RW, int WK, int J, int E>
+Variant skinny_variant() {
   Variant v{};
   const char* name = keep_name(std::string(E == kEngineF8 ? "f8" : "f16") + "_skinny_t" +
                                std::to_string(TMX) + "_r" + std::to_string(RW) + "_k" +
-                               std::to_string(WK) + "_s" + std::to_string(split));
-  v.cfg = GemmConfig{name, kSkinny, E, 0, 0, 0, 0, TMX, RW, WK, split};
-  v.fn[0] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, false, E>);
-  v.fn[1] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, true, E>);
+                               std::to_string(WK) + "_j" + std::to_string(J));
+  v.cfg = GemmConfig{name, kSkinny, E, 0, 0, 0, 0, TMX, RW, WK, J};
+  v.fn[0] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, J, false, E>);
+  v.fn[1] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, J, true, E>);
   v.threads = WK * 64;
-  v.lds = WK > 1 ? static_cast<size_t>(WK) * RW * TMX * 64 * 16 : 0;
+  v.lds = static_cast<size_t>(WK) * RW * TMX * 64 * 16;
   return v;
 }
 
@@ -600,28 +589,35 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineF8>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF8>());
     v.push_back(tiled_variant<256, 128, 4, 2, 3, kEngineF8>());
-#define FP8Q_SKINNY(T, R, W) \
-  for (int s : {1, 2, 4, 8}) v.push_back(skinny_variant<T, R, W, kEngineF16>(s));
-    FP8Q_SKINNY(1, 1, 4)
-    FP8Q_SKINNY(1, 1, 8)
-    FP8Q_SKINNY(1, 2, 4)
-    FP8Q_SKINNY(1, 2, 8)
-    FP8Q_SKINNY(1, 4, 4)
-    FP8Q_SKINNY(1, 4, 8)
-    FP8Q_SKINNY(2, 1, 4)
-    FP8Q_SKINNY(2, 1, 8)
-    FP8Q_SKINNY(2, 2, 4)
-    FP8Q_SKINNY(2, 2, 8)
-    FP8Q_SKINNY(2, 4, 4)
-    FP8Q_SKINNY(2, 4, 8)
-    FP8Q_SKINNY(4, 1, 4)
-    FP8Q_SKINNY(4, 1, 8)
-    FP8Q_SKINNY(4, 2, 4)
-    FP8Q_SKINNY(4, 2, 8)
-    FP8Q_SKINNY(4, 4, 4)
-    FP8Q_SKINNY(8, 1, 4)
-    FP8Q_SKINNY(8, 1, 8)
-    FP8Q_SKINNY(8, 2, 4)
+#define FP8Q_SKINNY(T, R, W, J) v.push_back(skinny_variant<T, R, W, J, kEngineF16>());
+    FP8Q_SKINNY(1, 1, 4, 1)
+    FP8Q_SKINNY(1, 2, 4, 1)
+    FP8Q_SKINNY(1, 2, 4, 2)
+    FP8Q_SKINNY(1, 4, 4, 2)
+    FP8Q_SKINNY(2, 1, 4, 2)
+    FP8Q_SKINNY(2, 2, 4, 2)
+    FP8Q_SKINNY(2, 4, 4, 2)
+    FP8Q_SKINNY(4, 1, 4, 1)
+    FP8Q_SKINNY(1, 1, 4, 2)
+    FP8Q_SKINNY(1, 1, 4, 4)
+    FP8Q_SKINNY(1, 1, 4, 8)
+    FP8Q_SKINNY(1, 2, 4, 4)
+    FP8Q_SKINNY(1, 2, 4, 8)
+    FP8Q_SKINNY(1, 4, 4, 4)
+    FP8Q_SKINNY(1, 1, 8, 4)
+    FP8Q_SKINNY(1, 2, 8, 4)
+    FP8Q_SKINNY(2, 1, 4, 4)
+    FP8Q_SKINNY(2, 1, 4, 8)
+    FP8Q_SKINNY(2, 2, 4, 4)
+    FP8Q_SKINNY(2, 2, 4, 8)
+    FP8Q_SKINNY(2, 1, 8, 4)
+    FP8Q_SKINNY(4, 1, 4, 2)
+    FP8Q_SKINNY(4, 1, 4, 4)
+    FP8Q_SKINNY(4, 2, 4, 2)
+    FP8Q_SKINNY(4, 2, 4, 4)
+    FP8Q_SKINNY(8, 1, 4, 2)
+    FP8Q_SKINNY(8, 1, 4, 4)
+    FP8Q_SKINNY(8, 2, 4, 2)
 #undef FP8Q_SKINNY
     return v;
   }();
@@ -655,10 +651,19 @@ bool gemm_config_fits(int id, long M, long N, long K) {
   return true;
 }
 
+// Workgroups along K for the skinny kernel: each covers wk*j K blocks.
+int skinny_split(const GemmConfig& c, long K) {
+  const long kb = K / kBK;
+  const long per = static_cast<long>(c.wk) * c.split;
+  return static_cast<int>((kb + per - 1) / per);
+}
+
 size_t gemm_workspace_bytes(int id, long M, long N, long K) {
   const GemmConfig& c = gemm_config(id);
-  if (c.kind != kSkinny || c.split <= 1) return 0;
-  return static_cast<size_t>(c.split) * M * N * sizeof(float);
+  if (c.kind != kSkinny) return 0;
+  const int split = skinny_split(c, K);
+  if (split <= 1) return 0;
+  return static_cast<size_t>(split) * M * N * sizeof(float);
 }
 
 hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, const float* sa,
@@ -672,7 +677,7 @@ hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, co
     void* args[] = {&y, &a, &sa, &b, &sb, &M, &N, &K};
     return hipLaunchKernel(v.fn[bw], dim3(tiles), dim3(v.threads), args, v.lds, st);
   }
-  int split = v.cfg.split;
+  int split = skinny_split(v.cfg, K);
   float* wsf = static_cast<float*>(ws);
   {
     void* args[] = {&y, &wsf, &a, &sa, &b, &sb, &M, &N, &K, &split};

@@ -96,12 +96,14 @@ def test_gemm_argument_checks():
     # a skinny variant cannot take more tokens than its fragment count
     sk = next(i for i in range(n) if "_skinny_t1_" in fq.fp8q_gemm_config_name(i))
     assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 17, 256, 256, None, 0, sk, None) == CFG
-    # split-K variant without a workspace
-    sp = next(i for i in range(n) if fq.fp8q_gemm_config_name(i).endswith("_s4"))
-    need = L.fp8q_workspace_size_cfg(sp, 8, 256, 1024)
+    # a skinny variant covering wk*j = 8 K blocks per workgroup needs a
+    # workspace of split = ceil(K/128 / 8) fp32 partials once K > 1024
+    sp = next(i for i in range(n) if fq.fp8q_gemm_config_name(i) == "f16_skinny_t1_r1_k4_j2")
+    assert L.fp8q_workspace_size_cfg(sp, 8, 256, 1024) == 0
+    need = L.fp8q_workspace_size_cfg(sp, 8, 256, 4096)
     assert need == 4 * 8 * 256 * 4
-    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 1024, None, 0, sp, None) == WS
-    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 1024, A, need - 1, sp, None) == WS
+    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 4096, None, 0, sp, None) == WS
+    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 4096, A, need - 1, sp, None) == WS
 
 
 def test_elementwise_argument_checks():
