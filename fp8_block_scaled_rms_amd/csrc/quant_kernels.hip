@@ -9,14 +9,19 @@
 // each with a per-token (one scale per row) or per-1x128-group scale.
 //
 // The work is HBM-bound (3 B per element for RMSNorm, 5 B per output element
-// for SiLU-and-mul), so the design is about streaming: a work unit is a whole
+// for SiLU-and-mul), so the design is about streaming.  A work unit is a whole
 // row (per-token mode, and RMSNorm, whose inverse RMS spans the row) or a
-// 2048*CH-column segment of a row (group mode).  A 256-thread workgroup owns a
-// unit; thread t owns the 8-element (16-byte) chunks t, t+256, ... so every
-// load and store is a coalesced 128-bit access, and the 16 consecutive lanes
-// that hold one 128-element group reduce its amax with four DPP moves.
-// Workgroups loop over units (grid-stride) so that per-workgroup set-up (the
-// SiLU table in LDS) is amortised.
+// 512*CH-column segment of a row (group mode).  A unit belongs to one 64-lane
+// wave -- rows up to 8192 columns and every group-mode segment -- so its
+// reductions are DPP/shuffle moves inside the wave with no barrier; longer
+// rows take the whole 256-thread workgroup and reduce across its waves in LDS.
+// Lane t of a unit owns the 8-element (16-byte) chunks t, t+TPR, ... and
+// issues all of their loads before any arithmetic, so every access is a
+// coalesced 128-bit one and each lane keeps up to 16 (x2 for the weight or
+// the up half) loads in flight.  The 16 consecutive lanes that hold one
+// 128-element group reduce its amax with four DPP moves.  Workgroups loop
+// over units (grid-stride) so per-workgroup set-up (the SiLU table in LDS) is
+// amortised.
 #include "fp8q_common.hpp"
 #include "quant_kernels.h"
 
@@ -26,7 +31,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;  // bf16 elements per 16-byte chunk
-constexpr int kSeg = kThreads * kChunk;  // columns covered per CH step
 
 // Correctly rounded SiLU over bf16 gates: table for |g| in [2^-25, 2^7),
 // closed rules outside it (silu(g) = g/2 exactly in fp32 below 2^-25;
@@ -52,94 +56,121 @@ __device__ __forceinline__ void load_silu_table(float* lds) {
   __syncthreads();
 }
 
-// Reduce across the 4 waves of the workgroup through LDS (fixed order).
-__device__ __forceinline__ double block_sum(double v, double* red) {
+// Reductions over the TPR threads of a unit: inside the wave first, then for
+// TPR = 128 / 256 across its 2 / 4 waves through LDS, in a fixed order.
+// Every wave of the workgroup must call these (they hold barriers when
+// TPR > 64).
+template <int TPR>
+__device__ __forceinline__ double unit_sum(double v, double* red) {
   v = sum64(v);
+  if constexpr (TPR == 64) return v;
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  double t = ((red[0] + red[1]) + red[2]) + red[3];
+  double t;
+  if constexpr (TPR == 128)
+    t = red[wave & ~1] + red[wave | 1];
+  else
+    t = ((red[0] + red[1]) + red[2]) + red[3];
   __syncthreads();
   return t;
 }
-__device__ __forceinline__ float block_max(float v, float* red) {
+template <int TPR>
+__device__ __forceinline__ float unit_max(float v, float* red) {
   v = max64(v);
+  if constexpr (TPR == 64) return v;
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float t;
+  if constexpr (TPR == 128)
+    t = fmaxf(red[wave & ~1], red[wave | 1]);
+  else
+    t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   return t;
 }
 
-template <int OP, int MODE, int CH>
+// A work unit is processed by TPR threads: one wave (TPR = 64; reductions
+// stay inside the wave, no barrier), two waves or the whole 256-thread
+// workgroup (TPR = 128 / 256: long rows, or few rows; cross-wave reductions
+// go through LDS).  Thread t of a unit owns the 8-element chunks t, t + TPR,
+// ..., CH of them.
+template <int OP, int MODE, int TPR, int CH>
 __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q,
                                                          float* __restrict__ scale,
                                                          const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w, int M,
                                                          int K, float eps) {
+  static_assert(TPR == 64 || TPR == 128 || TPR == kThreads, "unit = 1, 2 or 4 waves");
+  constexpr int kUnitsPerBlock = kThreads / TPR;
   __shared__ double red64[4];
   __shared__ float red32[4];
   extern __shared__ float silu_tab[];
   if constexpr (OP == kSilu) load_silu_table(silu_tab);
 
-  const int tid = threadIdx.x;
-  const int nchunk = K / kChunk;              // chunks per row
-  const int seg_cols = (MODE == kPerToken || OP == kRms) ? K : kSeg * CH;
-  const int nseg = (K + seg_cols - 1) / seg_cols;
+  const int sub = static_cast<int>(threadIdx.x) / TPR;
+  const int tid = static_cast<int>(threadIdx.x) % TPR;
+  const int nchunk = K / kChunk;  // chunks per row
+  constexpr bool kWholeRow = (MODE == kPerToken) || (OP == kRms);
+  const int unit_chunks = kWholeRow ? nchunk : TPR * CH;
+  const int nseg = (nchunk + unit_chunks - 1) / unit_chunks;
   const long units = static_cast<long>(M) * nseg;
   const long in_stride = (OP == kSilu) ? 2L * K : K;  // elements per input row
 
-  for (long unit = blockIdx.x; unit < units; unit += gridDim.x) {
+  for (long ub = blockIdx.x; ub * kUnitsPerBlock < units; ub += gridDim.x) {
+    // a unit past the end still takes part in the barriers, with no loads or
+    // stores
+    const long unit_raw = ub * kUnitsPerBlock + sub;
+    const bool active = unit_raw < units;
+    const long unit = active ? unit_raw : 0;
     const int row = static_cast<int>(unit / nseg);
     const int seg = static_cast<int>(unit % nseg);
-    const int c0 = seg * (seg_cols / kChunk);  // first chunk of this unit
+    const int c0 = seg * unit_chunks;  // first chunk of this unit
+    const int c_end = (c0 + unit_chunks < nchunk) ? c0 + unit_chunks : nchunk;
     const uint16_t* xr = x + row * in_stride;
 
-    // ---- load and front end: y (fp32) per element, kept in registers
-    float y[CH][kChunk];
+    // ---- load (all chunks first) and front end: y (fp32) per element
+    uint4 xv[CH], wv[CH];
     bool valid[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = c0 + tid + i * TPR;
+      valid[i] = active && c < c_end;
+      xv[i] = valid[i] ? *reinterpret_cast<const uint4*>(xr + c * kChunk) : make_uint4(0, 0, 0, 0);
+      if constexpr (OP == kRms)
+        wv[i] = valid[i] ? *reinterpret_cast<const uint4*>(w + c * kChunk) : make_uint4(0, 0, 0, 0);
+      if constexpr (OP == kSilu)
+        wv[i] = valid[i] ? *reinterpret_cast<const uint4*>(xr + K + c * kChunk)
+                         : make_uint4(0, 0, 0, 0);  // up
+    }
+    float y[CH][kChunk];
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = c0 + tid + i * kThreads;
-      valid[i] = (c < nchunk) && (c < c0 + seg_cols / kChunk);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (valid[i]) v = *reinterpret_cast<const uint4*>(xr + c * kChunk);
-      const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-      if constexpr (OP == kIdent) {
+      const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+      const uint32_t ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (OP == kIdent) {
           y[i][2 * j] = bf16_lo(vv[j]);
           y[i][2 * j + 1] = bf16_hi(vv[j]);
-        }
-      } else if constexpr (OP == kRms) {
-        uint4 wv = make_uint4(0, 0, 0, 0);
-        if (valid[i]) wv = *reinterpret_cast<const uint4*>(w + c * kChunk);
-        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        } else if constexpr (OP == kRms) {
           const float x0 = bf16_lo(vv[j]), x1 = bf16_hi(vv[j]);
           const double d0 = x0, d1 = x1;
           ss = fma(d0, d0, ss);
           ss = fma(d1, d1, ss);
-          y[i][2 * j] = x0 * bf16_lo(ww[j]);      // exact in fp32
+          y[i][2 * j] = x0 * bf16_lo(ww[j]);  // exact in fp32
           y[i][2 * j + 1] = x1 * bf16_hi(ww[j]);
-        }
-      } else {  // kSilu
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (valid[i]) u = *reinterpret_cast<const uint4*>(xr + K + c * kChunk);
-        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          y[i][2 * j] = silu_bf16(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(uu[j]);
-          y[i][2 * j + 1] = silu_bf16(vv[j] >> 16, silu_tab) * bf16_hi(uu[j]);
+        } else {  // kSilu: gate in xv, up in wv
+          y[i][2 * j] = silu_bf16(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(ww[j]);
+          y[i][2 * j + 1] = silu_bf16(vv[j] >> 16, silu_tab) * bf16_hi(ww[j]);
         }
       }
     }
 
     if constexpr (OP == kRms) {
-      const double tot = block_sum(ss, red64);
+      const double tot = unit_sum<TPR>(ss, red64);
       const double t = tot / static_cast<double>(K) + static_cast<double>(eps);
       const float inv = static_cast<float>(1.0 / sqrt(t));
 #pragma unroll
@@ -148,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
         for (int j = 0; j < kChunk; ++j) y[i][j] = y[i][j] * inv;
     }
 
-    // ---- amax per chunk, then per group (16 lanes) or per row (block)
+    // ---- amax per chunk, then per group (16 lanes) or per row
     float cmax[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -162,13 +193,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
       float m = cmax[0];
 #pragma unroll
       for (int i = 1; i < CH; ++i) m = fmaxf(m, cmax[i]);
-      const float amax = block_max(m, red32);
+      const float amax = unit_max<TPR>(m, red32);
       const GroupScale g = make_scale(amax);
-      if (tid == 0) scale[row] = g.s;
+      if (active && tid == 0) scale[row] = g.s;
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         if (!valid[i]) continue;
-        const int c = c0 + tid + i * kThreads;
+        const int c = c0 + tid + i * TPR;
         uint2 out;
         out.x = pack4_e4m3(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
                            quotient(y[i][3], g));
@@ -182,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
       for (int i = 0; i < CH; ++i) {
         const float amax = max16(cmax[i]);  // all 16 lanes of a group agree
         if (!valid[i]) continue;
-        const int c = c0 + tid + i * kThreads;
+        const int c = c0 + tid + i * TPR;
         const GroupScale g = make_scale(amax);
         if ((tid & 15) == 0) scale[static_cast<long>(row) * ngroups + c / 16] = g.s;
         uint2 out;
@@ -223,34 +254,45 @@ __global__ __launch_bounds__(kThreads) void silu_kernel(float* __restrict__ y,
 
 constexpr size_t kSiluLds = 8192 * sizeof(float);
 
-template <int OP, int MODE, int CH>
+template <int OP, int MODE, int TPR, int CH>
 hipError_t launch_quant_t(uint8_t* q, float* scale, const uint16_t* x, const uint16_t* w,
                           int M, int K, float eps, int grid, hipStream_t st) {
   const size_t lds = (OP == kSilu) ? kSiluLds : 0;
-  hipLaunchKernelGGL((quant_kernel<OP, MODE, CH>), dim3(grid), dim3(kThreads), lds, st, q,
+  hipLaunchKernelGGL((quant_kernel<OP, MODE, TPR, CH>), dim3(grid), dim3(kThreads), lds, st, q,
                      scale, x, w, M, K, eps);
   return hipGetLastError();
 }
 
-template <int OP, int MODE>
+template <int OP, int MODE, int TPR>
 hipError_t launch_quant_ch(int ch, uint8_t* q, float* scale, const uint16_t* x,
                            const uint16_t* w, int M, int K, float eps, int grid,
                            hipStream_t st) {
   switch (ch) {
-    case 1: return launch_quant_t<OP, MODE, 1>(q, scale, x, w, M, K, eps, grid, st);
-    case 2: return launch_quant_t<OP, MODE, 2>(q, scale, x, w, M, K, eps, grid, st);
-    case 3: return launch_quant_t<OP, MODE, 3>(q, scale, x, w, M, K, eps, grid, st);
-    case 4: return launch_quant_t<OP, MODE, 4>(q, scale, x, w, M, K, eps, grid, st);
-    case 6: return launch_quant_t<OP, MODE, 6>(q, scale, x, w, M, K, eps, grid, st);
-    case 8: return launch_quant_t<OP, MODE, 8>(q, scale, x, w, M, K, eps, grid, st);
-    case 12: return launch_quant_t<OP, MODE, 12>(q, scale, x, w, M, K, eps, grid, st);
-    case 16: return launch_quant_t<OP, MODE, 16>(q, scale, x, w, M, K, eps, grid, st);
+    case 1: return launch_quant_t<OP, MODE, TPR, 1>(q, scale, x, w, M, K, eps, grid, st);
+    case 2: return launch_quant_t<OP, MODE, TPR, 2>(q, scale, x, w, M, K, eps, grid, st);
+    case 4: return launch_quant_t<OP, MODE, TPR, 4>(q, scale, x, w, M, K, eps, grid, st);
+    case 6: return launch_quant_t<OP, MODE, TPR, 6>(q, scale, x, w, M, K, eps, grid, st);
+    case 8: return launch_quant_t<OP, MODE, TPR, 8>(q, scale, x, w, M, K, eps, grid, st);
+    case 10: return launch_quant_t<OP, MODE, TPR, 10>(q, scale, x, w, M, K, eps, grid, st);
+    case 12: return launch_quant_t<OP, MODE, TPR, 12>(q, scale, x, w, M, K, eps, grid, st);
+    case 16: return launch_quant_t<OP, MODE, TPR, 16>(q, scale, x, w, M, K, eps, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int OP, int MODE>
+hipError_t launch_quant_tpr(int tpr, int ch, uint8_t* q, float* scale, const uint16_t* x,
+                            const uint16_t* w, int M, int K, float eps, int grid,
+                            hipStream_t st) {
+  if (tpr == 64)
+    return launch_quant_ch<OP, MODE, 64>(ch, q, scale, x, w, M, K, eps, grid, st);
+  if (tpr == 128)
+    return launch_quant_ch<OP, MODE, 128>(ch, q, scale, x, w, M, K, eps, grid, st);
+  return launch_quant_ch<OP, MODE, kThreads>(ch, q, scale, x, w, M, K, eps, grid, st);
+}
+
 int pick_ch(int chunks_per_thread) {
-  static const int kAllowed[] = {1, 2, 3, 4, 6, 8, 12, 16};
+  static const int kAllowed[] = {1, 2, 4, 6, 8, 10, 12, 16};
   for (int c : kAllowed)
     if (c >= chunks_per_thread) return c;
   return -1;
@@ -258,33 +300,57 @@ int pick_ch(int chunks_per_thread) {
 
 }  // namespace
 
-int quant_max_k() { return kSeg * 16; }
+int quant_max_k() { return kThreads * kChunk * 16; }
 
 hipError_t launch_quant(int op, int mode, uint8_t* q, float* scale, const uint16_t* x,
                         const uint16_t* w, int M, int K, float eps, int num_cus,
                         hipStream_t st) {
-  // A row (or segment) is spread over 256 threads, CH 16-byte chunks each.
   const bool whole_row = (mode == kPerToken) || (op == kRms);
-  const int chunks = (K / kChunk + kThreads - 1) / kThreads;
-  const int ch = whole_row ? pick_ch(chunks) : 1;
+  const int nchunk = K / kChunk;
+  // Chunks a lane may hold before its registers cut occupancy too far (the
+  // SiLU front end keeps gate, up and the product live at once); measured
+  // per front end at the workload shapes.
+  const int ch_max = (op == kRms) ? 8 : (op == kSilu) ? 6 : 4;
+  // Waves wanted in flight before a unit is made smaller for parallelism.
+  const long want_waves = 16L * num_cus;
+  int tpr, ch, unit_chunks;
+  if (whole_row) {
+    // one wave per row while a lane holds at most ch_max chunks (and there
+    // are enough rows to fill the chip), else 2 or 4 waves per row
+    tpr = 64;
+    while (tpr < kThreads && ((nchunk + tpr - 1) / tpr > ch_max ||
+                              static_cast<long>(M) * (tpr / 64) < want_waves))
+      tpr *= 2;
+    ch = pick_ch((nchunk + tpr - 1) / tpr);
+    unit_chunks = nchunk;
+  } else {
+    // row segments of whole 128-column groups, one wave each: as few
+    // segments per row as ch_max allows, more when rows are few
+    tpr = 64;
+    int nseg = (nchunk + 64 * ch_max - 1) / (64 * ch_max);
+    while (static_cast<long>(M) * nseg < want_waves && nseg * 16 < nchunk) nseg *= 2;
+    ch = pick_ch((nchunk + nseg * 64 - 1) / (nseg * 64));
+    unit_chunks = 64 * ch;
+  }
   if (ch < 0) return hipErrorInvalidValue;
-  const int seg_cols = whole_row ? K : kSeg * ch;
-  const long units = static_cast<long>(M) * ((K + seg_cols - 1) / seg_cols);
-  const long cap = static_cast<long>(num_cus) * 8;
-  const int grid = static_cast<int>(units < cap ? units : cap);
+  const long units = static_cast<long>(M) * ((nchunk + unit_chunks - 1) / unit_chunks);
+  const long blocks = (units + (kThreads / tpr) - 1) / (kThreads / tpr);
+  // the SiLU table costs 32 KiB of LDS fill per workgroup: fewer, looping ones
+  const long cap = static_cast<long>(num_cus) * (op == kSilu ? 4 : 16);
+  const int grid = static_cast<int>(blocks < cap ? blocks : cap);
   if (op == kIdent) {
     return mode == kPerToken
-               ? launch_quant_ch<kIdent, kPerToken>(ch, q, scale, x, w, M, K, eps, grid, st)
-               : launch_quant_ch<kIdent, kGroup128>(ch, q, scale, x, w, M, K, eps, grid, st);
+               ? launch_quant_tpr<kIdent, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st)
+               : launch_quant_tpr<kIdent, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
   }
   if (op == kRms) {
     return mode == kPerToken
-               ? launch_quant_ch<kRms, kPerToken>(ch, q, scale, x, w, M, K, eps, grid, st)
-               : launch_quant_ch<kRms, kGroup128>(ch, q, scale, x, w, M, K, eps, grid, st);
+               ? launch_quant_tpr<kRms, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st)
+               : launch_quant_tpr<kRms, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
   }
   return mode == kPerToken
-             ? launch_quant_ch<kSilu, kPerToken>(ch, q, scale, x, w, M, K, eps, grid, st)
-             : launch_quant_ch<kSilu, kGroup128>(ch, q, scale, x, w, M, K, eps, grid, st);
+             ? launch_quant_tpr<kSilu, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st)
+             : launch_quant_tpr<kSilu, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
 }
 
 hipError_t launch_cvt_e4m3(uint8_t* q, const float* x, long n, int num_cus, hipStream_t st) {
