@@ -69,8 +69,57 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--detail", default=None, help="write a per-kernel breakdown JSON here")
-    p.add_argument("--cpu-sample-rows", type=int, default=512)
+    p.add_argument("--cpu-sample-rows", type=int, default=2048)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (3 times), the known-size "
+                        "reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+# HBM traffic of the dominant kernel, measured offline with rocprofv3 PMC
+# counters (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's
+# reading for a plain copy of known size).  The record names the kernel
+# variant, the shape and a hash of the kernel sources; when any of them
+# differs from the kernel measured now, the traffic is reported as null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_32b_prefill_gate_up_m8192.md")
+KERNEL_SOURCES = ("fp8_block_scaled_rms_amd/csrc/gemm_kernels.hip",
+                  "fp8_block_scaled_rms_amd/csrc/gemm_kernels.h",
+                  "fp8_block_scaled_rms_amd/csrc/fp8q_common.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(variant, op, M, N, K):
+    """Bytes per launch from the committed PMC record, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("traffic_record: "):
+                r = json.loads(line[len("traffic_record: "):])
+                if (r["variant"] == variant and (r["op"], r["M"], r["N"], r["K"]) == (op, M, N, K)
+                        and r["kernel_src_sha256_16"] == kernel_source_hash()):
+                    return int(r["bytes_per_launch"])
+    return None
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}), flush=True)
 
 
 class Step:
@@ -325,6 +374,9 @@ def main():
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     import fp8_block_scaled_rms_amd as fq
@@ -360,8 +412,12 @@ def main():
     if dom[2] > 0:
         achieved = dom[2] / dom_avg / 1e12
         peak = F16_PEAK_TFLOPS if exact else FP8_PEAK_TFLOPS
+        a_t, _, b_t, _ = step.operands[dominant]
+        traffic = measured_traffic(dom_cfg_name, MM if dom[1] == "scaled_mm" else BW,
+                                   a_t.shape[0], b_t.shape[0], a_t.shape[1])
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                "algorithmic_bytes": dom[3],
                 "kernel": dominant, "variant": dom_cfg_name,
                 "avg_launch_us": round(dom_avg * 1e6, 2),
                 "frac_of_fp8_peak": round(achieved / FP8_PEAK_TFLOPS, 4)}
