@@ -85,7 +85,7 @@ typedef enum { FP8Q_OP_SCALED_MM = 0, FP8Q_OP_SCALED_MM_BLOCKWISE = 1 } fp8q_gem
  *   w     [K]      bf16                  (in)
  *   eps   > 0, finite
  * Needs K > 0, K % 8 == 0 (PER_TOKEN) or K % 128 == 0 (GROUP128),
- * K <= 65536.
+ * K <= 32768.
  * ---------------------------------------------------------------------- */
 int fp8q_rmsnorm_quant(void* q, float* scale, const void* x, const void* w, int64_t M,
                        int64_t K, float eps, int mode, void* stream);
@@ -101,7 +101,7 @@ int fp8q_rmsnorm_quant(void* q, float* scale, const void* x, const void* w, int6
  *   scale   [M] or [M, D/128] fp32        (out)
  *   gate_up [M, 2D]  bf16, gate = columns [0,D), up = [D,2D)   (in)
  * Needs D > 0, D % 8 == 0 (PER_TOKEN) or D % 128 == 0 (GROUP128),
- * D <= 65536.
+ * D <= 32768.
  * ---------------------------------------------------------------------- */
 int fp8q_silu_mul_quant(void* q, float* scale, const void* gate_up, int64_t M, int64_t D,
                         int mode, void* stream);
