@@ -30,6 +30,14 @@ No bf16 rounding of y before quantization (the fusion removes it).
 SiLU-and-mul front end, per row of 2D (gate = columns [0,D), up = [D,2D)):
   y_i   = RN32(silu(g_i) * u_i),  silu correctly rounded to fp32 (oracle.silu)
 
+Two further scale rules (same quantizer otherwise):
+  power-of-two (UE8M0) scales, the format the page "Helion in vLLM: FP8
+  inference of Qwen3", section "Practical limits", names as required by
+  DeepGEMM on B200: scale = the smallest 2^e (e >= -127, the least UE8M0
+  value) with 448 * 2^e >= amax; an all-zero group therefore gets 2^-127.
+  static per-tensor scale: one caller-given scale s > 0 for the whole
+  tensor, q_i = E(RN32(y_i / s)) (no amax; the encoder saturates).
+
 Weight pre-quantization (inputs for the GEMMs, not on the hot path): the same
 quantizer per output channel (a row of W) or per 128x128 block of W[N,K].
 
@@ -51,7 +59,11 @@ from .silu import silu_bf16
 
 PER_TOKEN = 0
 GROUP128 = 1
+PER_TENSOR_STATIC = 2
+PER_TOKEN_UE8M0 = 3
+GROUP128_UE8M0 = 4
 GROUP = 128
+UE8M0_MIN_EXP = -127
 _F448 = np.float32(448.0)
 
 
@@ -77,22 +89,64 @@ def quantize_vectors(y) -> tuple[np.ndarray, np.ndarray]:
     return codes, scale
 
 
-def _quantize_rows(y: np.ndarray, mode: int) -> tuple[np.ndarray, np.ndarray]:
+def ue8m0_scale(amax) -> np.ndarray:
+    """Power-of-two scales: for each fp32 amax the smallest s = 2^e with
+    e >= -127 and 448 * s >= amax (exact comparisons in float64)."""
+    a = np.asarray(amax, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.float32)
+    for idx, v in np.ndenumerate(a):
+        v = float(v)
+        e = UE8M0_MIN_EXP
+        if v > 0.0:
+            # v < 2^p; 448 * 2^(p - 12) < 2^(p - 1) <= v, so start below the answer
+            e = max(UE8M0_MIN_EXP, math.frexp(v)[1] - 12)
+            while math.ldexp(448.0, e) < v:
+                e += 1
+        out[idx] = np.float32(math.ldexp(1.0, e))
+    return out
+
+
+def quantize_with_scale(y, scale) -> np.ndarray:
+    """q = E(RN32(y / s)) with a given positive scale s broadcast over the
+    last axis of y (s has y.shape[:-1], or is a scalar)."""
+    y = np.asarray(y, dtype=np.float32)
+    s = np.asarray(scale, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        qf = (y / (s[..., None] if s.ndim else s)).astype(np.float32)
+    return e4m3.encode(qf)
+
+
+def quantize_vectors_ue8m0(y) -> tuple[np.ndarray, np.ndarray]:
+    """Like quantize_vectors, with the power-of-two scale rule."""
+    y = np.asarray(y, dtype=np.float32)
+    amax = np.max(np.abs(y), axis=-1) if y.shape[-1] else np.zeros(y.shape[:-1], np.float32)
+    scale = ue8m0_scale(amax)
+    return quantize_with_scale(y, scale), scale
+
+
+def _quantize_rows(y: np.ndarray, mode: int, static_scale=None) -> tuple[np.ndarray, np.ndarray]:
     M, K = y.shape
-    if mode == PER_TOKEN:
-        return quantize_vectors(y)
-    if mode == GROUP128:
+    if mode in (PER_TOKEN, PER_TOKEN_UE8M0):
+        return (quantize_vectors if mode == PER_TOKEN else quantize_vectors_ue8m0)(y)
+    if mode in (GROUP128, GROUP128_UE8M0):
         if K % GROUP:
             raise ValueError("group128 quantization needs K % 128 == 0")
-        codes, scale = quantize_vectors(y.reshape(M, K // GROUP, GROUP))
+        fn = quantize_vectors if mode == GROUP128 else quantize_vectors_ue8m0
+        codes, scale = fn(y.reshape(M, K // GROUP, GROUP))
         return codes.reshape(M, K), scale.reshape(M, K // GROUP)
+    if mode == PER_TENSOR_STATIC:
+        s = np.float32(np.asarray(static_scale, dtype=np.float32).reshape(-1)[0])
+        if not (s > 0 and np.isfinite(s)):
+            raise ValueError("a static scale must be positive and finite")
+        return quantize_with_scale(y, s), np.array([s], dtype=np.float32)
     raise ValueError(f"unknown quantization mode {mode}")
 
 
-def quantize(x_bits, mode: int) -> tuple[np.ndarray, np.ndarray]:
-    """Standalone dynamic quantization of a bf16 [M,K] matrix (identity
-    front end): per token (scale [M]) or per 1x128 group (scale [M,K/128])."""
-    return _quantize_rows(_bf16_to_f32(x_bits), mode)
+def quantize(x_bits, mode: int, scale=None) -> tuple[np.ndarray, np.ndarray]:
+    """Standalone quantization of a bf16 [M,K] matrix (identity front end):
+    dynamic per token (scale [M]) or per 1x128 group (scale [M,K/128]), with
+    IEEE or power-of-two scales, or static per tensor with the given scale."""
+    return _quantize_rows(_bf16_to_f32(x_bits), mode, scale)
 
 
 def rms_inv(x_bits, eps: float) -> tuple[np.ndarray, np.ndarray]:
@@ -119,7 +173,7 @@ def rmsnorm_y(x_bits, w_bits, inv) -> np.ndarray:
 
 
 def rmsnorm_quant(x_bits, w_bits, eps: float, mode: int,
-                  inv_override=None) -> tuple[np.ndarray, np.ndarray]:
+                  inv_override=None, scale=None) -> tuple[np.ndarray, np.ndarray]:
     """Fused RMSNorm + dynamic FP8 quantization of bf16 x [M,K].
 
     inv_override (fp32 [M]) replaces the computed inverse RMS; it exists only
@@ -129,7 +183,7 @@ def rmsnorm_quant(x_bits, w_bits, eps: float, mode: int,
     if inv_override is not None:
         inv = np.asarray(inv_override, dtype=np.float32)
     y = rmsnorm_y(x_bits, w_bits, inv)
-    return _quantize_rows(y, mode)
+    return _quantize_rows(y, mode, scale)
 
 
 def silu_mul_y(gate_up_bits) -> np.ndarray:
@@ -142,12 +196,12 @@ def silu_mul_y(gate_up_bits) -> np.ndarray:
     return (s * u).astype(np.float32)
 
 
-def silu_mul_quant(gate_up_bits, mode: int) -> tuple[np.ndarray, np.ndarray]:
-    """Fused SiLU-and-mul + dynamic FP8 quantization of bf16 gate_up [M,2D]."""
+def silu_mul_quant(gate_up_bits, mode: int, scale=None) -> tuple[np.ndarray, np.ndarray]:
+    """Fused SiLU-and-mul + FP8 quantization of bf16 gate_up [M,2D]."""
     gu = np.asarray(gate_up_bits, dtype=np.uint16)
     if gu.shape[1] % 2:
         raise ValueError("gate_up must have an even number of columns")
-    return _quantize_rows(silu_mul_y(gu), mode)
+    return _quantize_rows(silu_mul_y(gu), mode, scale)
 
 
 def quant_weight_per_channel(W) -> tuple[np.ndarray, np.ndarray]:

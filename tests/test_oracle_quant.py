@@ -237,3 +237,113 @@ def test_weight_per_channel():
         amax = np.float32(np.max(np.abs(W[n])))
         assert scale[n] == np.float32(amax / np.float32(448))
         assert np.array_equal(codes[n], e4m3.encode((W[n] / scale[n]).astype(np.float32)))
+
+
+# ------------------------------------------------ power-of-two (UE8M0) scales
+
+def test_ue8m0_scale_closed_forms():
+    """Values fixed by the definition: the smallest 2^e (e >= -127) with
+    448 * 2^e >= amax."""
+    f = np.float32
+    above_448 = np.nextafter(f(448), f(1e9))
+    above_175 = np.nextafter(f(1.75), f(1e9))
+    cases = [(448.0, 1.0), (above_448, 2.0), (1.0, 2.0 ** -8), (1.75, 2.0 ** -8),
+             (above_175, 2.0 ** -7), (0.0, 2.0 ** -127), (1e-45, 2.0 ** -127),
+             (3.4e38, 2.0 ** 120), (224.0, 0.5), (56.0, 0.125)]
+    amax = np.array([c[0] for c in cases], np.float32)
+    want = np.array([c[1] for c in cases], np.float32)
+    assert np.array_equal(quant.ue8m0_scale(amax).view(np.uint32), want.view(np.uint32))
+
+
+def test_ue8m0_scale_properties():
+    rng = np.random.default_rng(11)
+    amax = (rng.random(5000) * np.exp2(rng.integers(-140, 120, 5000))).astype(np.float32)
+    s = quant.ue8m0_scale(amax).astype(np.float64)
+    m, e = np.frexp(s)
+    assert np.all(m == 0.5)                                   # a power of two
+    a = amax.astype(np.float64)
+    assert np.all(448.0 * s >= a)                             # covers amax
+    assert np.all((s == 2.0 ** -127) | (448.0 * s / 2 < a))   # and is the smallest
+
+
+def test_ue8m0_quantizer_invariants():
+    y = _groups(21)
+    codes, scale = quant.quantize_vectors_ue8m0(y)
+    rows = np.arange(len(y))
+    idx = np.argmax(np.abs(y), axis=1)
+    # amax / scale lies in (224, 448], so the amax element encodes to 0x76..0x7E
+    mag = codes[rows, idx] & 0x7F
+    assert np.all((mag >= 0x76) & (mag <= 0x7E))
+    # error of round-to-nearest at the code's own spacing
+    deq = e4m3.decode(codes) * scale.astype(np.float64)[:, None]
+    err = np.abs(deq - y.astype(np.float64))
+    bound = np.maximum(2.0 ** -4 * np.abs(y.astype(np.float64)),
+                       2.0 ** -10 * scale.astype(np.float64)[:, None]) * (1 + 2.0 ** -20)
+    assert np.all(err <= bound)
+    # power-of-two invariance: y * 2^j -> same codes, scale * 2^j
+    c2, s2 = quant.quantize_vectors_ue8m0((y * np.float32(2.0 ** 5)).astype(np.float32))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scale * np.float32(32))
+
+
+def test_ue8m0_equals_ieee_rule_when_amax_is_448_times_a_power_of_two():
+    """Where amax / 448 is itself a power of two both scale rules agree, so
+    the two quantizers must give the same bytes."""
+    y = _groups(22)
+    rows = np.arange(len(y))
+    idx = np.argmax(np.abs(y), axis=1)
+    target = np.exp2(np.floor(np.log2(np.abs(y[rows, idx]))) - 3).astype(np.float32) * np.float32(448)
+    z = np.clip(y, -target[:, None] * np.float32(0.99), target[:, None] * np.float32(0.99))
+    z[rows, idx] = np.where(y[rows, idx] < 0, -target, target)
+    c_ieee, s_ieee = quant.quantize_vectors(z)
+    c_ue8, s_ue8 = quant.quantize_vectors_ue8m0(z)
+    assert np.array_equal(s_ieee, s_ue8)
+    assert np.array_equal(c_ieee, c_ue8)
+
+
+def test_ue8m0_all_zero_group_and_layouts():
+    x = np.zeros((3, 256), np.float32)
+    x[1, 130] = -2.5
+    bits = synth.f32_to_bf16_bits(x)
+    q, s = quant.quantize(bits, quant.GROUP128_UE8M0)
+    assert s.shape == (3, 2)
+    assert s[0, 0] == np.float32(2.0 ** -127) and s[1, 1] == np.float32(2.0 ** -7)
+    assert q[1, 130] == 0xFA  # -2.5 / 2^-7 = -320 = -1.25 * 2^8: exponent 15, mantissa 2
+    assert np.all(q[0] == 0)
+    qt, st = quant.quantize(bits, quant.PER_TOKEN_UE8M0)
+    assert st.shape == (3,) and st[1] == np.float32(2.0 ** -7) and qt[1, 130] == 0xFA
+
+
+# ---------------------------------------------------- static per-tensor scale
+
+def test_static_scale_reduces_to_dynamic_and_to_plain_encode():
+    rng = synth.rng_for("static", 8, 512)
+    x = synth.gen_activations(rng, 8, 512)
+    # with the dynamic per-token scale of a one-row tensor the codes agree
+    q_dyn, s_dyn = quant.quantize(x[:1], quant.PER_TOKEN)
+    q_st, s_st = quant.quantize(x[:1], quant.PER_TENSOR_STATIC, scale=s_dyn)
+    assert np.array_equal(q_dyn, q_st) and s_st[0] == s_dyn[0]
+    # scale 1 is the plain encoder of the bf16 values
+    q1, _ = quant.quantize(x, quant.PER_TENSOR_STATIC, scale=np.float32(1.0))
+    assert np.array_equal(q1, e4m3.encode(synth.bf16_bits_to_f32(x)))
+
+
+def test_static_scale_saturates_and_keeps_zero_signs():
+    y = np.array([[1e30, -1e30, 448.0 * 3, -0.0, 0.0, 2.0 ** -20]], np.float32)
+    q, s = quant.quantize(synth.f32_to_bf16_bits(y), quant.PER_TENSOR_STATIC, scale=np.float32(2.0))
+    assert list(q[0][:5]) == [0x7E, 0xFE, 0x7E, 0x80, 0x00]
+    with pytest.raises(ValueError):
+        quant.quantize(synth.f32_to_bf16_bits(y), quant.PER_TENSOR_STATIC, scale=np.float32(0.0))
+
+
+def test_static_mode_on_fused_front_ends():
+    rng = synth.rng_for("static-fused", 4, 256)
+    x = synth.gen_activations(rng, 4, 256)
+    w = synth.gen_rms_weight(rng, 256)
+    inv, _ = quant.rms_inv(x, 1e-6)
+    y = quant.rmsnorm_y(x, w, inv)
+    q, s = quant.rmsnorm_quant(x, w, 1e-6, quant.PER_TENSOR_STATIC, scale=np.float32(0.01))
+    assert np.array_equal(q, e4m3.encode((y / np.float32(0.01)).astype(np.float32)))
+    gu = synth.gen_gate_up(rng, 4, 128)
+    q2, _ = quant.silu_mul_quant(gu, quant.PER_TENSOR_STATIC, scale=np.float32(0.5))
+    y2 = quant.silu_mul_y(gu)
+    assert np.array_equal(q2, e4m3.encode((y2 / np.float32(0.5)).astype(np.float32)))
