@@ -24,6 +24,9 @@ import torch
 
 PER_TOKEN = 0
 GROUP128 = 1
+PER_TENSOR_STATIC = 2
+PER_TOKEN_UE8M0 = 3
+GROUP128_UE8M0 = 4
 OP_SCALED_MM = 0
 OP_SCALED_MM_BLOCKWISE = 1
 
@@ -211,30 +214,45 @@ def fp8q_version() -> int:
 # --------------------------------------------------- allocating helpers --
 
 def _scale_shape(M: int, K: int, mode: int):
-    return (M,) if mode == PER_TOKEN else (M, K // 128)
+    if mode in (PER_TOKEN, PER_TOKEN_UE8M0):
+        return (M,)
+    if mode == PER_TENSOR_STATIC:
+        return (1,)
+    return (M, K // 128)
 
 
-def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, mode: int, stream=None):
+def _scale_arg(M, K, mode, scale, device):
+    """The scale tensor: allocated for the dynamic modes, the caller's
+    one-element fp32 tensor for the static mode."""
+    if mode == PER_TENSOR_STATIC:
+        if scale is None:
+            raise ValueError("the static mode needs scale=<one-element fp32 tensor>")
+        return scale
+    return torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=device)
+
+
+def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, mode: int, stream=None,
+                  scale=None):
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    s = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+    s = _scale_arg(M, K, mode, scale, x.device)
     fp8q_rmsnorm_quant(q, s, x, w, eps, mode, stream)
     return q, s
 
 
-def silu_mul_quant(gate_up: torch.Tensor, mode: int, stream=None):
+def silu_mul_quant(gate_up: torch.Tensor, mode: int, stream=None, scale=None):
     M, twoD = gate_up.shape
     D = twoD // 2
     q = torch.empty((M, D), dtype=torch.uint8, device=gate_up.device)
-    s = torch.empty(_scale_shape(M, D, mode), dtype=torch.float32, device=gate_up.device)
+    s = _scale_arg(M, D, mode, scale, gate_up.device)
     fp8q_silu_mul_quant(q, s, gate_up, mode, stream)
     return q, s
 
 
-def quant(x: torch.Tensor, mode: int, stream=None):
+def quant(x: torch.Tensor, mode: int, stream=None, scale=None):
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    s = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+    s = _scale_arg(M, K, mode, scale, x.device)
     fp8q_quant(q, s, x, mode, stream)
     return q, s
 

@@ -60,11 +60,12 @@ int launched(hipError_t e) {
 int check_quant_args(const void* q, const float* scale, const void* x, int64_t M, int64_t K,
                      int mode) {
   if (M < 0 || K <= 0) return FP8Q_ERR_INVALID_ARG;
-  if (mode != FP8Q_PER_TOKEN && mode != FP8Q_GROUP128) return FP8Q_ERR_BAD_MODE;
+  if (mode < FP8Q_PER_TOKEN || mode > FP8Q_GROUP128_UE8M0) return FP8Q_ERR_BAD_MODE;
   if (M == 0) return FP8Q_OK;
   if (!q || !scale || !x) return FP8Q_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(scale) || !aligned16(x)) return FP8Q_ERR_ALIGNMENT;
-  if (K % (mode == FP8Q_GROUP128 ? 128 : 8) != 0) return FP8Q_ERR_UNSUPPORTED_SHAPE;
+  const bool group = mode == FP8Q_GROUP128 || mode == FP8Q_GROUP128_UE8M0;
+  if (K % (group ? 128 : 8) != 0) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   if (K > fp8q::quant_max_k()) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   if (M > INT_MAX || M * K > (int64_t)1 << 40) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   return FP8Q_OK;

@@ -57,11 +57,51 @@ __device__ __forceinline__ GroupScale make_scale(float amax) {
   g.r = g.fast ? 1.0f / g.s : 1.0f;
   return g;
 }
+// Power-of-two (UE8M0) scale: the smallest s = 2^e, e >= -127, with
+// 448 * s >= amax.  For amax in [2^k, 2^(k+1)) that is 2^(k-8) when
+// amax <= 448 * 2^(k-8) = 1.75 * 2^k, else 2^(k-7); amax below 2^-126 (or
+// zero) gets the least UE8M0 value 2^-127.  The reciprocal is exact.
+__device__ __forceinline__ GroupScale make_scale_ue8m0(float amax) {
+  int e = -127;
+  if (amax >= 0x1p-126f) {
+    const uint32_t biased = (__float_as_uint(amax) >> 23) & 0xFFu;  // k + 127
+    const float bound = __uint_as_float((biased << 23) | 0x600000u);  // 1.75 * 2^k
+    const int k = static_cast<int>(biased) - 127;
+    e = (amax <= bound) ? k - 8 : k - 7;
+    if (e < -127) e = -127;
+  }
+  GroupScale g;
+  g.s = (e >= -126) ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23) : 0x1p-127f;
+  g.fast = g.s >= 0x1p-76f;
+  g.r = g.fast ? 1.0f / g.s : 1.0f;
+  return g;
+}
+
+// A caller-given (static) scale s > 0: the fast quotient where its proof
+// holds, IEEE division elsewhere.
+__device__ __forceinline__ GroupScale static_scale(float s) {
+  GroupScale g;
+  g.s = s;
+  g.fast = s >= 0x1p-76f && s < 0x1p126f;
+  g.r = g.fast ? 1.0f / s : 1.0f;
+  return g;
+}
+
 // y / s rounded to fp32; a zero scale (all-zero group) passes y (a signed
 // zero) through.
 __device__ __forceinline__ float quotient(float y, const GroupScale& g) {
   if (g.fast) return div_rn_corrected(y, g.s, g.r);
   return g.s == 0.0f ? y : y / g.s;
+}
+// The same for a static scale, where |y| may exceed 448 s by any factor: y
+// is first clamped to +-449 s (any quotient of magnitude >= 448 encodes to
+// +-448 anyway), which keeps the fast quotient inside its proven range.
+__device__ __forceinline__ float quotient_static(float y, const GroupScale& g) {
+  if (g.fast) {
+    const float lim = 449.0f * g.s;
+    return div_rn_corrected(__builtin_amdgcn_fmed3f(y, -lim, lim), g.s, g.r);
+  }
+  return y / g.s;
 }
 
 // ------------------------------------------------------------- e4m3 --

@@ -7,12 +7,23 @@
 namespace fp8q {
 
 enum QuantOp { kIdent = 0, kRms = 1, kSilu = 2 };
-enum QuantMode { kPerToken = 0, kGroup128 = 1 };
+// Values equal the fp8q_quant_mode values of the C ABI.
+enum QuantMode {
+  kPerToken = 0,      // dynamic, one scale per row, scale = amax / 448
+  kGroup128 = 1,      // dynamic, one scale per 1x128 group
+  kStaticTensor = 2,  // caller-given scale[0] for the whole tensor (input)
+  kPerTokenUe8 = 3,   // per row, power-of-two scale
+  kGroup128Ue8 = 4    // per 1x128 group, power-of-two scale
+};
+constexpr bool mode_is_row(int m) { return m == kPerToken || m == kPerTokenUe8; }
+constexpr bool mode_is_group(int m) { return m == kGroup128 || m == kGroup128Ue8; }
+constexpr bool mode_is_ue8(int m) { return m == kPerTokenUe8 || m == kGroup128Ue8; }
 
 // Largest K (columns of the quantized output) a launch supports.
 int quant_max_k();
 
-// q [M,K] e4m3, scale [M] or [M,K/128]; x is [M,K] bf16 (kIdent, kRms) or
+// q [M,K] e4m3, scale [M] or [M,K/128] (written) or [1] (kStaticTensor:
+// read); x is [M,K] bf16 (kIdent, kRms) or
 // gate_up [M,2K] bf16 (kSilu); w [K] bf16 (kRms only).
 hipError_t launch_quant(int op, int mode, uint8_t* q, float* scale, const uint16_t* x,
                         const uint16_t* w, int M, int K, float eps, int num_cus,

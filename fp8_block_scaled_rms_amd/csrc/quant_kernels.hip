@@ -6,12 +6,14 @@
 //   kIdent  dynamic_per_token_scaled_fp8_quant / per_token_group_fp8_quant
 //   kRms    rms_norm_dynamic_per_token_quant   / rms_norm_per_block_quant
 //   kSilu   silu_and_mul_dynamic_per_token_quant / silu_and_mul_per_block_quant
-// each with a per-token (one scale per row) or per-1x128-group scale.
+// each with a per-token (one scale per row) or per-1x128-group scale, the
+// scale being amax/448 or the power of two UE8M0 needs (page above, section
+// "Practical limits"), or with one caller-given static scale per tensor.
 //
 // The work is HBM-bound (3 B per element for RMSNorm, 5 B per output element
 // for SiLU-and-mul), so the design is about streaming.  A work unit is a whole
 // row (per-token mode, and RMSNorm, whose inverse RMS spans the row) or a
-// 512*CH-column segment of a row (group mode).  A unit belongs to one 64-lane
+// 512*CH-column segment of a row (group and static modes).  A unit belongs to one 64-lane
 // wave -- rows up to 8192 columns and every group-mode segment -- so its
 // reductions are DPP/shuffle moves inside the wave with no barrier; longer
 // rows take the whole 256-thread workgroup and reduce across its waves in LDS.
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
   const int sub = static_cast<int>(threadIdx.x) / TPR;
   const int tid = static_cast<int>(threadIdx.x) % TPR;
   const int nchunk = K / kChunk;  // chunks per row
-  constexpr bool kWholeRow = (MODE == kPerToken) || (OP == kRms);
+  constexpr bool kWholeRow = mode_is_row(MODE) || (OP == kRms);
   const int unit_chunks = kWholeRow ? nchunk : TPR * CH;
   const int nseg = (nchunk + unit_chunks - 1) / unit_chunks;
   const long units = static_cast<long>(M) * nseg;
@@ -189,12 +191,12 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
       cmax[i] = valid[i] ? m : 0.0f;
     }
 
-    if constexpr (MODE == kPerToken) {
+    if constexpr (mode_is_row(MODE)) {
       float m = cmax[0];
 #pragma unroll
       for (int i = 1; i < CH; ++i) m = fmaxf(m, cmax[i]);
       const float amax = unit_max<TPR>(m, red32);
-      const GroupScale g = make_scale(amax);
+      const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
       if (active && tid == 0) scale[row] = g.s;
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -207,20 +209,33 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
                            quotient(y[i][7], g));
         *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
       }
-    } else {
+    } else if constexpr (mode_is_group(MODE)) {
       const int ngroups = K / kGroup;
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const float amax = max16(cmax[i]);  // all 16 lanes of a group agree
         if (!valid[i]) continue;
         const int c = c0 + tid + i * TPR;
-        const GroupScale g = make_scale(amax);
+        const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
         if ((tid & 15) == 0) scale[static_cast<long>(row) * ngroups + c / 16] = g.s;
         uint2 out;
         out.x = pack4_e4m3(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
                            quotient(y[i][3], g));
         out.y = pack4_e4m3(quotient(y[i][4], g), quotient(y[i][5], g), quotient(y[i][6], g),
                            quotient(y[i][7], g));
+        *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
+      }
+    } else {  // kStaticTensor: the caller's scale, read once per unit
+      const GroupScale g = static_scale(scale[0]);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (!valid[i]) continue;
+        const int c = c0 + tid + i * TPR;
+        uint2 out;
+        out.x = pack4_e4m3(quotient_static(y[i][0], g), quotient_static(y[i][1], g),
+                           quotient_static(y[i][2], g), quotient_static(y[i][3], g));
+        out.y = pack4_e4m3(quotient_static(y[i][4], g), quotient_static(y[i][5], g),
+                           quotient_static(y[i][6], g), quotient_static(y[i][7], g));
         *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
       }
     }
@@ -280,15 +295,40 @@ hipError_t launch_quant_ch(int ch, uint8_t* q, float* scale, const uint16_t* x,
   }
 }
 
+// Units of more than one wave only exist for whole-row units (per-token
+// modes and RMSNorm); other combinations instantiate the one-wave kernel only.
 template <int OP, int MODE>
 hipError_t launch_quant_tpr(int tpr, int ch, uint8_t* q, float* scale, const uint16_t* x,
                             const uint16_t* w, int M, int K, float eps, int grid,
                             hipStream_t st) {
   if (tpr == 64)
     return launch_quant_ch<OP, MODE, 64>(ch, q, scale, x, w, M, K, eps, grid, st);
-  if (tpr == 128)
-    return launch_quant_ch<OP, MODE, 128>(ch, q, scale, x, w, M, K, eps, grid, st);
-  return launch_quant_ch<OP, MODE, kThreads>(ch, q, scale, x, w, M, K, eps, grid, st);
+  if constexpr (mode_is_row(MODE) || OP == kRms) {
+    if (tpr == 128)
+      return launch_quant_ch<OP, MODE, 128>(ch, q, scale, x, w, M, K, eps, grid, st);
+    return launch_quant_ch<OP, MODE, kThreads>(ch, q, scale, x, w, M, K, eps, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int OP>
+hipError_t launch_quant_mode(int mode, int tpr, int ch, uint8_t* q, float* scale,
+                             const uint16_t* x, const uint16_t* w, int M, int K, float eps,
+                             int grid, hipStream_t st) {
+  switch (mode) {
+    case kPerToken:
+      return launch_quant_tpr<OP, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    case kGroup128:
+      return launch_quant_tpr<OP, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    case kStaticTensor:
+      return launch_quant_tpr<OP, kStaticTensor>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    case kPerTokenUe8:
+      return launch_quant_tpr<OP, kPerTokenUe8>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    case kGroup128Ue8:
+      return launch_quant_tpr<OP, kGroup128Ue8>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 int pick_ch(int chunks_per_thread) {
@@ -305,7 +345,7 @@ int quant_max_k() { return kThreads * kChunk * 16; }
 hipError_t launch_quant(int op, int mode, uint8_t* q, float* scale, const uint16_t* x,
                         const uint16_t* w, int M, int K, float eps, int num_cus,
                         hipStream_t st) {
-  const bool whole_row = (mode == kPerToken) || (op == kRms);
+  const bool whole_row = mode_is_row(mode) || (op == kRms);
   const int nchunk = K / kChunk;
   // Chunks a lane may hold before its registers cut occupancy too far (the
   // SiLU front end keeps gate, up and the product live at once); measured
@@ -338,19 +378,11 @@ hipError_t launch_quant(int op, int mode, uint8_t* q, float* scale, const uint16
   // the SiLU table costs 32 KiB of LDS fill per workgroup: fewer, looping ones
   const long cap = static_cast<long>(num_cus) * (op == kSilu ? 4 : 16);
   const int grid = static_cast<int>(blocks < cap ? blocks : cap);
-  if (op == kIdent) {
-    return mode == kPerToken
-               ? launch_quant_tpr<kIdent, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st)
-               : launch_quant_tpr<kIdent, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
-  }
-  if (op == kRms) {
-    return mode == kPerToken
-               ? launch_quant_tpr<kRms, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st)
-               : launch_quant_tpr<kRms, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
-  }
-  return mode == kPerToken
-             ? launch_quant_tpr<kSilu, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st)
-             : launch_quant_tpr<kSilu, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+  if (op == kIdent)
+    return launch_quant_mode<kIdent>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+  if (op == kRms)
+    return launch_quant_mode<kRms>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+  return launch_quant_mode<kSilu>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
 }
 
 hipError_t launch_cvt_e4m3(uint8_t* q, const float* x, long n, int num_cus, hipStream_t st) {

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_VERSION 100 /* major*100 + minor */
+#define FP8Q_VERSION 101 /* major*100 + minor */
 
 typedef enum {
   FP8Q_OK = 0,
@@ -63,9 +63,22 @@ typedef enum {
   FP8Q_ERR_BAD_CONFIG = 9         /* unknown or inapplicable GEMM config  */
 } fp8q_status;
 
+/* Quantization modes.  Dynamic modes compute the scale from the data and
+ * WRITE it to `scale`; the static mode READS scale[0].
+ *   amax/448 rule:  scale = RN32(amax / 448)
+ *   UE8M0 rule:     scale = the smallest 2^e, e >= -127, with 448 * 2^e >= amax
+ *                   (power-of-two scales, the format the page "Helion in
+ *                   vLLM: FP8 inference of Qwen3", section "Practical
+ *                   limits", names for DeepGEMM on B200); an all-zero group
+ *                   gets 2^-127.
+ * Codes are always q = e4m3(RN32(y / scale)), saturating. */
 typedef enum {
-  FP8Q_PER_TOKEN = 0, /* one scale per row:       scale [M]         */
-  FP8Q_GROUP128 = 1   /* one scale per 1x128:     scale [M, K/128]  */
+  FP8Q_PER_TOKEN = 0,          /* one scale per row,    amax/448: scale [M]        (out) */
+  FP8Q_GROUP128 = 1,           /* one scale per 1x128,  amax/448: scale [M, K/128] (out) */
+  FP8Q_PER_TENSOR_STATIC = 2,  /* caller's scale for all elements: scale [1]      (in)
+                                  scale[0] must be positive and finite             */
+  FP8Q_PER_TOKEN_UE8M0 = 3,    /* one power-of-two scale per row:  scale [M]       (out) */
+  FP8Q_GROUP128_UE8M0 = 4      /* one power-of-two scale per 1x128: [M, K/128]     (out) */
 } fp8q_quant_mode;
 
 typedef enum { FP8Q_OP_SCALED_MM = 0, FP8Q_OP_SCALED_MM_BLOCKWISE = 1 } fp8q_gemm_op;
@@ -77,14 +90,14 @@ typedef enum { FP8Q_OP_SCALED_MM = 0, FP8Q_OP_SCALED_MM_BLOCKWISE = 1 } fp8q_gem
  *   inv  = RN32(1 / sqrt(sum_k x[m,k]^2 / K + eps))   sum in fp64, the rest
  *                                                      in IEEE fp64
  *   y    = RN32(RN32(x[m,k] * w[k]) * inv)             no bf16 rounding of y
- *   then the quantizer per row (PER_TOKEN) or per 1x128 group (GROUP128).
+ *   then the quantizer of `mode` (fp8q_quant_mode).
  *
  *   q     [M, K]   e4m3 bytes            (out)
- *   scale [M] or [M, K/128] fp32         (out)
+ *   scale fp32, shape and direction by mode (fp8q_quant_mode)
  *   x     [M, K]   bf16                  (in)
  *   w     [K]      bf16                  (in)
  *   eps   > 0, finite
- * Needs K > 0, K % 8 == 0 (PER_TOKEN) or K % 128 == 0 (GROUP128),
+ * Needs K > 0, K % 128 == 0 for the GROUP128 modes, K % 8 == 0 otherwise,
  * K <= 32768.
  * ---------------------------------------------------------------------- */
 int fp8q_rmsnorm_quant(void* q, float* scale, const void* x, const void* w, int64_t M,
@@ -98,19 +111,19 @@ int fp8q_rmsnorm_quant(void* q, float* scale, const void* x, const void* w, int6
  *            rounded to fp32; then the quantizer as above.
  *
  *   q       [M, D]   e4m3 bytes           (out)
- *   scale   [M] or [M, D/128] fp32        (out)
+ *   scale   fp32, shape and direction by mode (fp8q_quant_mode)
  *   gate_up [M, 2D]  bf16, gate = columns [0,D), up = [D,2D)   (in)
- * Needs D > 0, D % 8 == 0 (PER_TOKEN) or D % 128 == 0 (GROUP128),
+ * Needs D > 0, D % 128 == 0 for the GROUP128 modes, D % 8 == 0 otherwise,
  * D <= 32768.
  * ---------------------------------------------------------------------- */
 int fp8q_silu_mul_quant(void* q, float* scale, const void* gate_up, int64_t M, int64_t D,
                         int mode, void* stream);
 
 /* ------------------------------------------------------------------------
- * Standalone dynamic FP8 quantization of a bf16 matrix
- * (dynamic_per_token_scaled_fp8_quant / per_token_group_fp8_quant):
- * the quantizer with an identity front end.  Arguments as for
- * fp8q_rmsnorm_quant without w and eps.
+ * Standalone FP8 quantization of a bf16 matrix
+ * (dynamic_per_token_scaled_fp8_quant / per_token_group_fp8_quant, and the
+ * static per-tensor form): the quantizer with an identity front end.
+ * Arguments as for fp8q_rmsnorm_quant without w and eps.
  * ---------------------------------------------------------------------- */
 int fp8q_quant(void* q, float* scale, const void* x, int64_t M, int64_t K, int mode,
                void* stream);

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_version() == 100
+    assert L.fp8q_version() == 101
     for s in range(10):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"
@@ -54,7 +54,12 @@ def test_quant_argument_checks():
     rms = L.fp8q_rmsnorm_quant
     assert rms(A, B, C, D, -1, 256, 1e-6, 1, None) == INVALID
     assert rms(A, B, C, D, 4, 0, 1e-6, 1, None) == INVALID
-    assert rms(A, B, C, D, 4, 256, 1e-6, 2, None) == MODE
+    assert rms(A, B, C, D, 4, 256, 1e-6, 5, None) == MODE
+    assert rms(A, B, C, D, 4, 256, 1e-6, -1, None) == MODE
+    assert rms(A, B, C, D, 4, 200, 1e-6, 4, None) == SHAPE       # K % 128 (group, UE8M0)
+    assert rms(A, B, C, D, 4, 200, 1e-6, 3, None) != SHAPE       # K % 8 suffices per token
+    assert rms(A, B, C, D, 4, 200, 1e-6, 2, None) != SHAPE       # and for the static mode
+    assert rms(A, 0, C, D, 4, 256, 1e-6, 2, None) == INVALID     # static mode reads scale
     assert rms(A, B, C, D, 0, 256, 1e-6, 1, None) == OK          # M == 0: no-op
     assert rms(0, 0, 0, 0, 0, 256, 1e-6, 1, None) == OK          # not inspected
     assert rms(0, B, C, D, 4, 256, 1e-6, 1, None) == INVALID

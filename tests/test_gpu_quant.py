@@ -31,13 +31,20 @@ def _rows_sample(M, n=192):
     return np.sort(np.concatenate([[0, M - 1], rest]))
 
 
-def _check_rms(x, w, mode, rows=None, eps=EPS):
+def _static(scale):
+    return None if scale is None else f32_dev(np.array([scale], np.float32))
+
+
+def _check_rms(x, w, mode, rows=None, eps=EPS, scale=None):
     M, K = x.shape
-    q, s = fq.rmsnorm_quant(bf16_dev(x), bf16_dev(w), eps, mode)
+    q, s = fq.rmsnorm_quant(bf16_dev(x), bf16_dev(w), eps, mode, scale=_static(scale))
     torch.cuda.synchronize()
     q, s = host(q), host(s)
     rows = np.arange(M) if rows is None else rows
-    qr, sr = quant.rmsnorm_quant(x[rows], w, eps, mode)
+    qr, sr = quant.rmsnorm_quant(x[rows], w, eps, mode, scale=scale)
+    if mode == fq.PER_TENSOR_STATIC:  # the scale is an input: one value, all rows
+        s = np.repeat(s, M)
+        sr = np.repeat(sr, len(rows))
     qg, sg = q[rows], s[rows]
     bad = [i for i in range(len(rows))
            if not (np.array_equal(qg[i], qr[i]) and np.array_equal(sg[i].view(np.uint32),
@@ -50,7 +57,8 @@ def _check_rms(x, w, mode, rows=None, eps=EPS):
             mid = (float(lo) + float(other)) / 2
             assert abs(inv64[j] - mid) <= 2.0 ** -40 * inv64[j], f"row {rows[i]} differs"
             q2, s2 = quant.rmsnorm_quant(x[rows[i]:rows[i] + 1], w, eps, mode,
-                                         inv_override=np.array([other], np.float32))
+                                         inv_override=np.array([other], np.float32),
+                                         scale=scale)
             assert np.array_equal(qg[i], q2[0]) and np.array_equal(sg[i], s2[0]), f"row {rows[i]}"
     return len(bad)
 
@@ -115,15 +123,18 @@ def test_rmsnorm_quant_edge_rows():
         _check_rms(x, w, mode, eps=1e-30)
 
 
-def _check_silu(gu, mode, rows=None):
+def _check_silu(gu, mode, rows=None, scale=None):
     M, twoD = gu.shape
-    q, s = fq.silu_mul_quant(bf16_dev(gu), mode)
+    q, s = fq.silu_mul_quant(bf16_dev(gu), mode, scale=_static(scale))
     torch.cuda.synchronize()
     q, s = host(q), host(s)
     rows = np.arange(M) if rows is None else rows
-    qr, sr = quant.silu_mul_quant(gu[rows], mode)
+    qr, sr = quant.silu_mul_quant(gu[rows], mode, scale=scale)
     assert np.array_equal(q[rows], qr)
-    assert np.array_equal(s[rows].view(np.uint32), sr.view(np.uint32))
+    if mode == fq.PER_TENSOR_STATIC:
+        assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    else:
+        assert np.array_equal(s[rows].view(np.uint32), sr.view(np.uint32))
 
 
 SILU_CASES = [
@@ -258,3 +269,76 @@ def test_quant_writes_stay_in_bounds():
         torch.cuda.synchronize()
         assert torch.all(qbuf[:256] == 0xA5) and torch.all(qbuf[256 + M * K:] == 0xA5)
         assert torch.all(sbuf[:64] == -7.0) and torch.all(sbuf[64 + ns:] == -7.0)
+
+
+# ------------------------------------------- UE8M0 and static scale modes
+
+UE8_CASES = [
+    ("c2-per-token", 16, 2048, fq.PER_TOKEN_UE8M0),
+    ("c2-per-token", 2048, 2048, fq.PER_TOKEN_UE8M0),
+    ("c3-group", 32, 4096, fq.GROUP128_UE8M0),
+    ("c4-group", 2048, 5120, fq.GROUP128_UE8M0),
+    ("ragged", 37, 5120, fq.PER_TOKEN_UE8M0),
+    ("ragged", 5, 128, fq.GROUP128_UE8M0),
+    ("max-k", 4, 32768, fq.PER_TOKEN_UE8M0),
+    ("max-k", 4, 32768, fq.GROUP128_UE8M0),
+]
+
+
+@pytest.mark.parametrize("name,M,K,mode", UE8_CASES)
+def test_rmsnorm_quant_ue8m0_parity(name, M, K, mode):
+    say("rmsnorm_quant ue8m0", name, M, K, mode)
+    rng = synth.rng_for(name, "rmsnorm_quant", M, K)
+    x = synth.gen_activations(rng, M, K)
+    w = synth.gen_rms_weight(rng, K)
+    _check_rms(x, w, mode)
+
+
+@pytest.mark.parametrize("name,M,D,mode", [("c3-group", 32, 12288, fq.GROUP128_UE8M0),
+                                           ("c5-group", 64, 25600, fq.GROUP128_UE8M0),
+                                           ("c2-per-token", 128, 6144, fq.PER_TOKEN_UE8M0),
+                                           ("ragged", 9, 1000, fq.PER_TOKEN_UE8M0)])
+def test_silu_mul_quant_ue8m0_parity(name, M, D, mode):
+    say("silu_mul_quant ue8m0", name, M, D, mode)
+    rng = synth.rng_for(name, "silu_mul_quant", M, D)
+    gu = synth.gen_gate_up(rng, M, D)
+    _check_silu(gu, mode)
+
+
+@pytest.mark.parametrize("scale", [0.05, 3.0e-3, 1.0e-30, 7.0e37, 1.0])
+def test_static_scale_parity(scale):
+    """Static per-tensor scale on all three front ends, scales on the fast
+    quotient path (0.05, 3e-3, 1) and on the IEEE-division path (1e-30,
+    7e37), with inputs that saturate."""
+    M, K = 48, 2056
+    say("static", scale)
+    rng = synth.rng_for("static", M, K)
+    x = synth.gen_activations(rng, M, K)
+    w = synth.gen_rms_weight(rng, K)
+    _check_rms(x, w, fq.PER_TENSOR_STATIC, scale=np.float32(scale))
+    gu = synth.gen_gate_up(rng, M, K)
+    _check_silu(gu, fq.PER_TENSOR_STATIC, scale=np.float32(scale))
+    q, _ = fq.quant(bf16_dev(x), fq.PER_TENSOR_STATIC, scale=_static(np.float32(scale)))
+    torch.cuda.synchronize()
+    qr, _ = quant.quantize(x, fq.PER_TENSOR_STATIC, scale=np.float32(scale))
+    assert np.array_equal(host(q), qr)
+
+
+@pytest.mark.parametrize("mode", [fq.PER_TOKEN_UE8M0, fq.GROUP128_UE8M0])
+def test_ue8m0_edge_rows(mode):
+    """All-zero, tiny, huge and one-hot rows (scale 2^-127, the subnormal
+    quotient path and the largest exponents)."""
+    K = 256
+    rng = synth.rng_for("edge-ue8", K)
+    w = synth.gen_rms_weight(rng, K)
+    rows = [np.zeros(K, np.float32), np.full(K, -3.0e-30, np.float32),
+            np.full(K, 1.0e30, np.float32)]
+    t = np.zeros(K, np.float32); t[5] = 1e-35; rows.append(t)
+    o = np.zeros(K, np.float32); o[200] = -5.0; rows.append(o)
+    x = synth.f32_to_bf16_bits(np.stack(rows))
+    _check_rms(x, w, mode)
+    q, s = fq.quant(bf16_dev(x), mode)
+    torch.cuda.synchronize()
+    qr, sr = quant.quantize(x, mode)
+    assert np.array_equal(host(q), qr)
+    assert np.array_equal(host(s).view(np.uint32), sr.view(np.uint32))
