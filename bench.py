@@ -26,7 +26,9 @@ value = GEMM FLOPs of one step / wall time of one step (quantizer kernels
 included in the time).  The roofline entry is for the dominant kernel (the
 largest share of step time), timed with HIP events on its launch stream
 during the timed steps.  The CPU baseline runs the oracle on a bounded
-sample of that kernel's workload.
+sample of that kernel's workload.  After the timed region, decode_chain
+reports the Qwen3-8B decode layer's 8-launch chain per M, launched eagerly
+and replayed from a HIP graph.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -368,6 +370,49 @@ def cpu_baseline(step: Step, label: str, rows: int):
                       f"N={N}, K={K}: fp64 dequantized matmul, {dt:.1f} s"}
 
 
+def decode_chain_latency(step: Step, Ms=(1, 8, 32), reps: int = 50):
+    """The Qwen3-8B block-decode layer chain (8 launches) per M, launched
+    eagerly through the C ABI and replayed from a HIP graph: the time per
+    chain back to back (between two events on the current stream), and the
+    wall-clock latency of one chain from an idle GPU (issue, then
+    synchronize; median of 20)."""
+    from fp8_block_scaled_rms_amd.graph import LinearChain
+
+    torch = step.torch
+    mode, hidden, (qkv_n, o_k, gu_n, inter), _ = WORKLOADS["qwen3-8b-block-decode"]
+    wts = {"qkv": step.weight(qkv_n, hidden, mode), "o_proj": step.weight(hidden, o_k, mode),
+           "gate_up": step.weight(gu_n, hidden, mode), "down": step.weight(hidden, inter, mode)}
+    rw = (1.0 + step.randn((hidden,), 0.1)).to(torch.bfloat16)
+    out = {"workload": "qwen3-8b-block-decode", "launches_per_chain": 8}
+    for M in Ms:
+        chain = LinearChain(step.activations(M, hidden), step.activations(M, o_k),
+                            step.activations(M, hidden), rw, wts, mode)
+        chain.capture()
+        res = {}
+        for kind, fn in (("eager_us", chain.run), ("graph_us", chain.replay)):
+            for _ in range(3):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[kind] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+            lat = []
+            for _ in range(20):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                lat.append(time.perf_counter() - t0)
+            res[kind.replace("_us", "_single_us")] = round(float(np.median(lat)) * 1e6, 1)
+        out[f"M{M}"] = res
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -441,6 +486,8 @@ def main():
                    "gemm_us": round(s["gemm_us"], 1), "quant_us": round(s["quant_us"], 1)}
               for wl, s in summary.items()}
 
+    chain = decode_chain_latency(step)
+
     cpu = None
     if not args.no_cpu_baseline and dom[2] > 0:
         cpu = cpu_baseline(step, dominant, args.cpu_sample_rows)
@@ -468,6 +515,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_workload": per_wl,
+        "decode_chain": chain,
     }
     if args.detail:
         detail = {label: {"kind": kind, "us": round(kt[label], 2), "flops": flops,
