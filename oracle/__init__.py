@@ -21,12 +21,13 @@ Modules
   silu   -- correctly rounded fp32 SiLU over every bf16 input
   gemm   -- fp64 dequantized matmuls (scaled_mm, scaled_mm_blockwise) and the
             GEMM acceptance rule
+  int8   -- W8A8 INT8: symmetric int8 quantizers and the exact-integer GEMM
 
 Every function here is pinned by a test under tests/ against something other
 than itself (library routines, exhaustive enumeration, closed forms, exact
 rational arithmetic); see each module's docstring.
 """
-from . import e4m3, quant, silu, gemm  # noqa: F401
+from . import e4m3, quant, silu, gemm, int8  # noqa: F401
 
 PER_TOKEN = 0
 GROUP128 = 1
