@@ -13,7 +13,8 @@ allocate the outputs and the workspace with torch and call them.
 
 Data types: bf16 tensors are torch.bfloat16; e4m3 tensors are torch.uint8
 (raw OCP e4m3 bytes; ``t.view(torch.float8_e4m3fn)`` reinterprets them);
-scales are torch.float32.
+int8 tensors (the W8A8 INT8 functions, *_int8) are torch.int8; scales are
+torch.float32.
 """
 from __future__ import annotations
 
@@ -29,6 +30,7 @@ PER_TOKEN_UE8M0 = 3
 GROUP128_UE8M0 = 4
 OP_SCALED_MM = 0
 OP_SCALED_MM_BLOCKWISE = 1
+OP_SCALED_MM_INT8 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8q.so")
@@ -60,6 +62,12 @@ SIGNATURES = {
     "fp8q_scaled_mm_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT, _P]),
     "fp8q_scaled_mm_blockwise_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ,
                                             _INT, _P]),
+    "fp8q_rmsnorm_quant_int8": (_INT, [_P, _P, _P, _P, _I64, _I64, _F32, _INT, _P]),
+    "fp8q_silu_mul_quant_int8": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
+    "fp8q_quant_int8": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
+    "fp8q_scaled_mm_int8": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "fp8q_scaled_mm_int8_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT,
+                                       _P]),
     "fp8q_cvt_e4m3": (_INT, [_P, _P, _I64, _P]),
     "fp8q_silu": (_INT, [_P, _P, _I64, _P]),
     "fp8q_status_string": (ctypes.c_char_p, [_INT]),
@@ -120,6 +128,7 @@ def _need(t: torch.Tensor, dtypes, what: str):
 
 
 _E4M3 = (torch.uint8, torch.float8_e4m3fn)
+_I8 = (torch.int8,)
 _BF16 = (torch.bfloat16,)
 _F32T = (torch.float32,)
 
@@ -176,6 +185,42 @@ def fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws=None, cfg: int | None = None,
         rc = lib().fp8q_scaled_mm_blockwise_cfg(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M,
                                                 N, K, _ptr(ws), wsb, cfg, _stream(stream))
     _check(rc, "fp8q_scaled_mm_blockwise")
+
+
+def fp8q_rmsnorm_quant_int8(q, scale, x, w, eps: float, mode: int, stream=None) -> None:
+    _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x"); _need(w, _BF16, "w")
+    M, K = x.shape
+    _check(lib().fp8q_rmsnorm_quant_int8(_ptr(q), _ptr(scale), _ptr(x), _ptr(w), M, K, eps, mode,
+                                         _stream(stream)), "fp8q_rmsnorm_quant_int8")
+
+
+def fp8q_silu_mul_quant_int8(q, scale, gate_up, mode: int, stream=None) -> None:
+    _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(gate_up, _BF16, "gate_up")
+    M, twoD = gate_up.shape
+    _check(lib().fp8q_silu_mul_quant_int8(_ptr(q), _ptr(scale), _ptr(gate_up), M, twoD // 2,
+                                          mode, _stream(stream)), "fp8q_silu_mul_quant_int8")
+
+
+def fp8q_quant_int8(q, scale, x, mode: int, stream=None) -> None:
+    _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x")
+    M, K = x.shape
+    _check(lib().fp8q_quant_int8(_ptr(q), _ptr(scale), _ptr(x), M, K, mode, _stream(stream)),
+           "fp8q_quant_int8")
+
+
+def fp8q_scaled_mm_int8(y, a, b, sa, sb, ws=None, cfg: int | None = None, stream=None) -> None:
+    _need(y, _BF16, "y"); _need(a, _I8, "a"); _need(b, _I8, "b")
+    _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    if cfg is None:
+        rc = lib().fp8q_scaled_mm_int8(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K,
+                                       _ptr(ws), wsb, _stream(stream))
+    else:
+        rc = lib().fp8q_scaled_mm_int8_cfg(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N,
+                                           K, _ptr(ws), wsb, cfg, _stream(stream))
+    _check(rc, "fp8q_scaled_mm_int8")
 
 
 def fp8q_workspace_size(op: int, M: int, N: int, K: int, cfg: int | None = None) -> int:
@@ -255,6 +300,41 @@ def quant(x: torch.Tensor, mode: int, stream=None, scale=None):
     s = _scale_arg(M, K, mode, scale, x.device)
     fp8q_quant(q, s, x, mode, stream)
     return q, s
+
+
+def _int8_out(M, K, mode, scale, device):
+    q = torch.empty((M, K), dtype=torch.int8, device=device)
+    if mode == PER_TENSOR_STATIC:
+        if scale is None:
+            raise ValueError("the static mode needs scale=<one-element fp32 tensor>")
+        return q, scale
+    return q, torch.empty((M,), dtype=torch.float32, device=device)
+
+
+def rmsnorm_quant_int8(x, w, eps: float, mode: int, stream=None, scale=None):
+    q, s = _int8_out(x.shape[0], x.shape[1], mode, scale, x.device)
+    fp8q_rmsnorm_quant_int8(q, s, x, w, eps, mode, stream)
+    return q, s
+
+
+def silu_mul_quant_int8(gate_up, mode: int, stream=None, scale=None):
+    q, s = _int8_out(gate_up.shape[0], gate_up.shape[1] // 2, mode, scale, gate_up.device)
+    fp8q_silu_mul_quant_int8(q, s, gate_up, mode, stream)
+    return q, s
+
+
+def quant_int8(x, mode: int, stream=None, scale=None):
+    q, s = _int8_out(x.shape[0], x.shape[1], mode, scale, x.device)
+    fp8q_quant_int8(q, s, x, mode, stream)
+    return q, s
+
+
+def scaled_mm_int8(a, b, sa, sb, cfg: int | None = None, stream=None):
+    M, N = a.shape[0], b.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    ws = _workspace(OP_SCALED_MM_INT8, M, N, a.shape[1], a.device, cfg)
+    fp8q_scaled_mm_int8(y, a, b, sa, sb, ws, cfg, stream)
+    return y
 
 
 def _workspace(op, M, N, K, device, cfg=None):

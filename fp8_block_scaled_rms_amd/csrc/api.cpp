@@ -58,9 +58,11 @@ int launched(hipError_t e) {
 }
 
 int check_quant_args(const void* q, const float* scale, const void* x, int64_t M, int64_t K,
-                     int mode) {
+                     int mode, int fmt) {
   if (M < 0 || K <= 0) return FP8Q_ERR_INVALID_ARG;
   if (mode < FP8Q_PER_TOKEN || mode > FP8Q_GROUP128_UE8M0) return FP8Q_ERR_BAD_MODE;
+  if (fmt == fp8q::kFmtI8 && mode != FP8Q_PER_TOKEN && mode != FP8Q_PER_TENSOR_STATIC)
+    return FP8Q_ERR_BAD_MODE;
   if (M == 0) return FP8Q_OK;
   if (!q || !scale || !x) return FP8Q_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(scale) || !aligned16(x)) return FP8Q_ERR_ALIGNMENT;
@@ -71,19 +73,19 @@ int check_quant_args(const void* q, const float* scale, const void* x, int64_t M
   return FP8Q_OK;
 }
 
-int run_quant(int op, void* q, float* scale, const void* x, const void* w, int64_t M, int64_t K,
-              float eps, int mode, void* stream) {
+int run_quant(int op, int fmt, void* q, float* scale, const void* x, const void* w, int64_t M,
+              int64_t K, float eps, int mode, void* stream) {
   int num_cus = 0;
   int rc = device_check(&num_cus);
   if (rc != FP8Q_OK) return rc;
-  return launched(fp8q::launch_quant(op, mode, static_cast<uint8_t*>(q), scale,
+  return launched(fp8q::launch_quant(op, mode, fmt, static_cast<uint8_t*>(q), scale,
                                      static_cast<const uint16_t*>(x),
                                      static_cast<const uint16_t*>(w), static_cast<int>(M),
                                      static_cast<int>(K), eps, num_cus,
                                      static_cast<hipStream_t>(stream)));
 }
 
-int check_gemm_args(const void* y, const void* a, const void* b, const float* sa,
+int check_gemm_args(int op, const void* y, const void* a, const void* b, const float* sa,
                     const float* sb, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N <= 0 || K <= 0) return FP8Q_ERR_INVALID_ARG;
   if (M == 0) return FP8Q_OK;
@@ -92,16 +94,19 @@ int check_gemm_args(const void* y, const void* a, const void* b, const float* sa
     return FP8Q_ERR_ALIGNMENT;
   if (K % 128 != 0 || N % 128 != 0) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return FP8Q_ERR_UNSUPPORTED_SHAPE;
+  // int32 sums of int8 products stay exact for K * 127^2 < 2^31
+  if (op == FP8Q_OP_SCALED_MM_INT8 && K > 131072) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   return FP8Q_OK;
 }
 
 int run_gemm(int op, void* y, const void* a, const float* sa, const void* b, const float* sb,
              int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, int cfg,
              void* stream) {
-  int rc = check_gemm_args(y, a, b, sa, sb, M, N, K);
+  int rc = check_gemm_args(op, y, a, b, sa, sb, M, N, K);
   if (rc != FP8Q_OK || M == 0) return rc;
   if (cfg < 0) cfg = fp8q::dispatch_gemm(op, M, N, K);
-  if (cfg < 0 || cfg >= fp8q::gemm_num_configs() || !fp8q::gemm_config_fits(cfg, M, N, K))
+  if (cfg < 0 || cfg >= fp8q::gemm_num_configs() || !fp8q::variant_serves(cfg, op) ||
+      !fp8q::gemm_config_fits(cfg, M, N, K))
     return FP8Q_ERR_BAD_CONFIG;
   const size_t need = fp8q::gemm_workspace_bytes(cfg, M, N, K);
   if (need > 0) {
@@ -118,32 +123,72 @@ int run_gemm(int op, void* y, const void* a, const float* sa, const void* b, con
       static_cast<hipStream_t>(stream)));
 }
 
+int rmsnorm_quant_any(int fmt, void* q, float* scale, const void* x, const void* w, int64_t M,
+                      int64_t K, float eps, int mode, void* stream) {
+  int rc = check_quant_args(q, scale, x, M, K, mode, fmt);
+  if (rc != FP8Q_OK || M == 0) return rc;
+  if (!w) return FP8Q_ERR_INVALID_ARG;
+  if (!aligned16(w)) return FP8Q_ERR_ALIGNMENT;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return FP8Q_ERR_INVALID_ARG;
+  return run_quant(fp8q::kRms, fmt, q, scale, x, w, M, K, eps, mode, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
 int fp8q_rmsnorm_quant(void* q, float* scale, const void* x, const void* w, int64_t M,
                        int64_t K, float eps, int mode, void* stream) {
-  int rc = check_quant_args(q, scale, x, M, K, mode);
-  if (rc != FP8Q_OK || M == 0) return rc;
-  if (!w) return FP8Q_ERR_INVALID_ARG;
-  if (!aligned16(w)) return FP8Q_ERR_ALIGNMENT;
-  if (!(eps > 0.0f) || !std::isfinite(eps)) return FP8Q_ERR_INVALID_ARG;
-  return run_quant(fp8q::kRms, q, scale, x, w, M, K, eps, mode, stream);
+  return rmsnorm_quant_any(fp8q::kFmtE4m3, q, scale, x, w, M, K, eps, mode, stream);
 }
 
 int fp8q_silu_mul_quant(void* q, float* scale, const void* gate_up, int64_t M, int64_t D,
                         int mode, void* stream) {
-  int rc = check_quant_args(q, scale, gate_up, M, D, mode);
+  int rc = check_quant_args(q, scale, gate_up, M, D, mode, fp8q::kFmtE4m3);
   if (rc != FP8Q_OK || M == 0) return rc;
-  return run_quant(fp8q::kSilu, q, scale, gate_up, nullptr, M, D, 0.0f, mode, stream);
+  return run_quant(fp8q::kSilu, fp8q::kFmtE4m3, q, scale, gate_up, nullptr, M, D, 0.0f, mode,
+                   stream);
 }
 
 int fp8q_quant(void* q, float* scale, const void* x, int64_t M, int64_t K, int mode,
                void* stream) {
-  int rc = check_quant_args(q, scale, x, M, K, mode);
+  int rc = check_quant_args(q, scale, x, M, K, mode, fp8q::kFmtE4m3);
   if (rc != FP8Q_OK || M == 0) return rc;
-  return run_quant(fp8q::kIdent, q, scale, x, nullptr, M, K, 0.0f, mode, stream);
+  return run_quant(fp8q::kIdent, fp8q::kFmtE4m3, q, scale, x, nullptr, M, K, 0.0f, mode,
+                   stream);
+}
+
+int fp8q_rmsnorm_quant_int8(void* q, float* scale, const void* x, const void* w, int64_t M,
+                            int64_t K, float eps, int mode, void* stream) {
+  return rmsnorm_quant_any(fp8q::kFmtI8, q, scale, x, w, M, K, eps, mode, stream);
+}
+
+int fp8q_silu_mul_quant_int8(void* q, float* scale, const void* gate_up, int64_t M,
+                             int64_t D, int mode, void* stream) {
+  int rc = check_quant_args(q, scale, gate_up, M, D, mode, fp8q::kFmtI8);
+  if (rc != FP8Q_OK || M == 0) return rc;
+  return run_quant(fp8q::kSilu, fp8q::kFmtI8, q, scale, gate_up, nullptr, M, D, 0.0f, mode,
+                   stream);
+}
+
+int fp8q_quant_int8(void* q, float* scale, const void* x, int64_t M, int64_t K, int mode,
+                    void* stream) {
+  int rc = check_quant_args(q, scale, x, M, K, mode, fp8q::kFmtI8);
+  if (rc != FP8Q_OK || M == 0) return rc;
+  return run_quant(fp8q::kIdent, fp8q::kFmtI8, q, scale, x, nullptr, M, K, 0.0f, mode,
+                   stream);
+}
+
+int fp8q_scaled_mm_int8(void* y, const void* a, const void* b, const float* sa,
+                        const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return run_gemm(FP8Q_OP_SCALED_MM_INT8, y, a, sa, b, sb, M, N, K, ws, ws_bytes, -1, stream);
+}
+
+int fp8q_scaled_mm_int8_cfg(void* y, const void* a, const void* b, const float* sa,
+                            const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                            size_t ws_bytes, int cfg, void* stream) {
+  return run_gemm(FP8Q_OP_SCALED_MM_INT8, y, a, sa, b, sb, M, N, K, ws, ws_bytes, cfg, stream);
 }
 
 int fp8q_scaled_mm(void* y, const void* a, const void* b, const float* sa, const float* sb,
@@ -173,7 +218,9 @@ int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const float* sa, const 
 
 size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  if (op != FP8Q_OP_SCALED_MM && op != FP8Q_OP_SCALED_MM_BLOCKWISE) return 0;
+  if (op != FP8Q_OP_SCALED_MM && op != FP8Q_OP_SCALED_MM_BLOCKWISE &&
+      op != FP8Q_OP_SCALED_MM_INT8)
+    return 0;
   const int cfg = fp8q::dispatch_gemm(op, M, N, K);
   return cfg < 0 ? 0 : fp8q::gemm_workspace_bytes(cfg, M, N, K);
 }

@@ -33,40 +33,51 @@ int find_variant(const char* name) {
   return -1;
 }
 
-int find_skinny(int tm, int rw, int wk, int j) {
+int find_skinny(int engine, int tm, int rw, int wk, int j) {
   const int n = gemm_num_configs();
   for (int i = 0; i < n; ++i) {
     const GemmConfig& c = gemm_config(i);
-    if (c.kind == kSkinny && c.engine == kEngineExact && c.tm == tm && c.rw == rw &&
-        c.wk == wk && c.split == j)
+    if (c.kind == kSkinny && c.engine == engine && c.tm == tm && c.rw == rw && c.wk == wk &&
+        c.split == j)
       return i;
   }
   return -1;
 }
 
-// Fixed rule for shapes without a measured row (exact engine only): the
-// weight-streaming kernel up to 128 tokens, the tiled kernel above.
+// Fixed rule for shapes without a measured row (exact FP8 engine, or the
+// int8 engine for op 2): the weight-streaming kernel up to 128 tokens, the
+// tiled kernel above.
 int rule(int op, long M, long N, long K) {
-  (void)op;
   (void)K;
+  const int engine = op == kOpInt8 ? kEngineInt8 : kEngineExact;
   if (M <= 128) {
     const int tm = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     const int rw = (N >= 8192 && N % 32 == 0) ? 2 : 1;
-    const int j = tm <= 2 ? 8 : tm == 4 ? 4 : 2;
-    const int id = find_skinny(tm, rw, 4, j);
+    const int j = tm <= 2 ? (engine == kEngineInt8 ? 4 : 8) : tm == 4 ? 4 : 2;
+    int id = find_skinny(engine, tm, rw, 4, j);
+    if (id < 0) id = find_skinny(engine, tm, 1, 4, j);
+    if (id < 0) id = find_skinny(engine, tm, 1, 4, 2);
     if (id >= 0) return id;
   }
-  if (N % 128 == 0) return find_variant("f16_tiled_m128_n128_w2x2_st2");
+  if (N % 128 == 0)
+    return find_variant(engine == kEngineInt8 ? "i8_tiled_m128_n128_w2x2_st2"
+                                              : "f16_tiled_m128_n128_w2x2_st2");
   return -1;
 }
 
 }  // namespace
 
+bool variant_serves(int id, int op) {
+  if (id < 0 || id >= gemm_num_configs()) return false;
+  const bool i8 = gemm_config(id).engine == kEngineInt8;
+  return op == kOpInt8 ? i8 : (op == kOpScaledMm || op == kOpBlockwise) && !i8;
+}
+
 int dispatch_gemm(int op, long M, long N, long K) {
   for (const TableRow* r = kTable; r->variant != nullptr; ++r) {
     if (r->op == op && r->n == N && r->k == K && M <= r->m_max) {
       const int id = find_variant(r->variant);
-      if (id >= 0 && gemm_config_fits(id, M, N, K)) return id;
+      if (id >= 0 && variant_serves(id, op) && gemm_config_fits(id, M, N, K)) return id;
       break;
     }
   }

@@ -57,6 +57,15 @@ __device__ __forceinline__ GroupScale make_scale(float amax) {
   g.r = g.fast ? 1.0f / g.s : 1.0f;
   return g;
 }
+// Symmetric int8 scale amax / 127 (W8A8 INT8).
+__device__ __forceinline__ GroupScale make_scale_i8(float amax) {
+  GroupScale g;
+  g.s = amax / 127.0f;  // IEEE division
+  g.fast = g.s >= 0x1p-76f;
+  g.r = g.fast ? 1.0f / g.s : 1.0f;
+  return g;
+}
+
 // Power-of-two (UE8M0) scale: the smallest s = 2^e, e >= -127, with
 // 448 * s >= amax.  For amax in [2^k, 2^(k+1)) that is 2^(k-8) when
 // amax <= 448 * 2^(k-8) = 1.75 * 2^k, else 2^(k-7); amax below 2^-126 (or
@@ -116,6 +125,18 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
   return static_cast<uint32_t>(v);
+}
+
+// ------------------------------------------------------------- int8 --
+// Four fp32 quotients -> four int8 bytes: round to nearest even (the
+// default rounding mode), saturating to +-127.  Clamping first is the same
+// as clamping after: +-127 are integers.
+__device__ __forceinline__ uint32_t i8_byte(float v) {
+  const float r = __builtin_rintf(__builtin_amdgcn_fmed3f(v, -127.0f, 127.0f));
+  return static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d) {
+  return i8_byte(a) | (i8_byte(b) << 8) | (i8_byte(c) << 16) | (i8_byte(d) << 24);
 }
 
 // ------------------------------------------------------ reductions --

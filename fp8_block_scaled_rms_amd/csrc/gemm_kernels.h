@@ -21,8 +21,10 @@ namespace fp8q {
 enum GemmKind { kTiled = 0, kSkinny = 1 };
 
 // Accumulation engine (see gemm_kernels.hip): 0 = FP8 MFMA (fast, hardware
-// group-truncated sums), 1 = exact f16 MFMA on losslessly widened operands.
-enum GemmEngine { kEngineFp8 = 0, kEngineExact = 1 };
+// group-truncated sums), 1 = exact f16 MFMA on losslessly widened operands,
+// 2 = int8 MFMA with exact int32 sums (W8A8 INT8 operands, per-token x
+// per-channel scales only).
+enum GemmEngine { kEngineFp8 = 0, kEngineExact = 1, kEngineInt8 = 2 };
 
 struct GemmConfig {
   const char* name;
@@ -41,7 +43,8 @@ bool gemm_config_fits(int id, long M, long N, long K);
 size_t gemm_workspace_bytes(int id, long M, long N, long K);
 
 // blockwise == false: per-token x per-channel scales (sa [M], sb [N]);
-// blockwise == true : sa [M, K/128], sb [N/128, K/128].
+// blockwise == true : sa [M, K/128], sb [N/128, K/128] (not for kEngineInt8).
+// The operand bytes are e4m3 codes, or int8 values for a kEngineInt8 variant.
 hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, const float* sa,
                        const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
                        hipStream_t st);

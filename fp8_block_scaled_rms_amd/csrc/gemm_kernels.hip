@@ -47,6 +47,7 @@ namespace fp8q {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -71,8 +72,37 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 // Both engines use the same 32-byte-per-lane fragments; kEngineF16 feeds
 // instruction s with bytes [8s, 8s+8) of each lane's 32, identically for both
 // operands, which is a fixed permutation of K inside the block.
+//
+// kEngineI8 (W8A8 INT8, per-token x per-channel only): the operands are int8
+// and the block is two v_mfma_i32_16x16x64_i8 (bytes [0,16) and [16,32) of
+// each lane's 32), accumulated exactly in int32 across all of K; the
+// epilogue converts to fp32 and applies the scales.
 constexpr int kEngineF8 = kEngineFp8;
 constexpr int kEngineF16 = kEngineExact;
+constexpr int kEngineI8 = kEngineInt8;
+
+// Accumulator of one 16x16 tile in a lane: 4 fp32, or 4 int32 (kEngineI8).
+template <int E>
+struct AccT {
+  typedef v4f T;
+};
+template <>
+struct AccT<kEngineI8> {
+  typedef v4i T;
+};
+template <int E>
+__device__ __forceinline__ typename AccT<E>::T acc_zero() {
+  typename AccT<E>::T z;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) z[r] = 0;
+  return z;
+}
+__device__ __forceinline__ v4f to_f32(v4f a) { return a; }
+__device__ __forceinline__ v4f to_f32(v4i a) { return __builtin_convertvector(a, v4f); }
+
+constexpr const char* engine_prefix(int e) {
+  return e == kEngineF8 ? "f8" : e == kEngineF16 ? "f16" : "i8";
+}
 
 __device__ __forceinline__ v8h widen8(int lo, int hi) {
   const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
@@ -97,12 +127,19 @@ template <>
 struct Frag<kEngineF16> {
   v8h h[4];
 };
+template <>
+struct Frag<kEngineI8> {
+  v4i lo, hi;
+};
 
 template <int E>
 __device__ __forceinline__ Frag<E> prep(const v8i& raw) {
   Frag<E> f;
   if constexpr (E == kEngineF8) {
     f.b = raw;
+  } else if constexpr (E == kEngineI8) {
+    f.lo = v4i{raw[0], raw[1], raw[2], raw[3]};
+    f.hi = v4i{raw[4], raw[5], raw[6], raw[7]};
   } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) f.h[s] = widen8(raw[2 * s], raw[2 * s + 1]);
@@ -112,8 +149,12 @@ __device__ __forceinline__ Frag<E> prep(const v8i& raw) {
 
 // c + W_block * X_block^T for one tile (weights on the 16-row side).
 template <int E>
-__device__ __forceinline__ v4f block_mma(const Frag<E>& w, const Frag<E>& x, v4f c) {
-  if constexpr (E == kEngineF8) {
+__device__ __forceinline__ typename AccT<E>::T block_mma(const Frag<E>& w, const Frag<E>& x,
+                                                         typename AccT<E>::T c) {
+  if constexpr (E == kEngineI8) {
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(w.lo, x.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(w.hi, x.hi, c, 0, 0, 0);
+  } else if constexpr (E == kEngineF8) {
     // operand formats 0 = e4m3; scale 127 = E8M0 2^0 on both sides
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.b, x.b, c, 0, 0, 0, 127, 0, 127);
   } else {
@@ -310,11 +351,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       g2lds4(s_src + s_off + kb, lds0 + buf * S::kStage + S::kXBytes + S::kWBytes + wave * 256);
   };
 
-  v4f acc[S::kFW][S::kFT];
+  static_assert(!(BLOCK && E == kEngineI8), "the int8 engine is per-token x per-channel only");
+  typename AccT<E>::T acc[S::kFW][S::kFT];
 #pragma unroll
   for (int i = 0; i < S::kFW; ++i)
 #pragma unroll
-    for (int t = 0; t < S::kFT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < S::kFT; ++t) acc[i][t] = acc_zero<E>();
 
 #pragma unroll
   for (int p = 0; p < ST - 1; ++p)
@@ -355,7 +397,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) {
         if constexpr (BLOCK) {
-          const v4f p = block_mma<E>(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f p = block_mma<E>(wf, xf[t], acc_zero<E>());
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
         } else {
@@ -375,7 +417,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < S::kFW; ++i) {
       const int n = n0 + wn * S::kTN + 16 * i + 4 * g;
-      v4f v = acc[i][t];
+      v4f v = to_f32(acc[i][t]);
       if constexpr (!BLOCK) {
         const float4 s4 = *reinterpret_cast<const float4*>(sb + n);
         v[0] = v[0] * sm * s4.x;
@@ -445,11 +487,13 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
     }
   }
 
-  v4f acc[RW][TMX];
+  static_assert(!(BLOCK && E == kEngineI8), "the int8 engine is per-token x per-channel only");
+  typedef typename AccT<E>::T Acc;
+  Acc acc[RW][TMX];
 #pragma unroll
   for (int i = 0; i < RW; ++i)
 #pragma unroll
-    for (int t = 0; t < TMX; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TMX; ++t) acc[i][t] = acc_zero<E>();
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     if (kb0 + WK * j >= KB) break;
@@ -462,7 +506,7 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
 #pragma unroll
       for (int t = 0; t < TMX; ++t) {
         if constexpr (BLOCK) {
-          const v4f p = block_mma<E>(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f p = block_mma<E>(wf, xf[t], acc_zero<E>());
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[j][t], acc[i][t][r]);
         } else {
@@ -472,9 +516,9 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
     }
   }
 
-  // add the WK waves' partial sums in a fixed order
+  // add the WK waves' partial sums in a fixed order (int32 sums are exact)
   constexpr int kFrags = RW * TMX;
-  v4f* r4 = reinterpret_cast<v4f*>(red);
+  Acc* r4 = reinterpret_cast<Acc*>(red);
 #pragma unroll
   for (int i = 0; i < RW; ++i)
 #pragma unroll
@@ -482,15 +526,16 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
   __syncthreads();
   for (int f = wave; f < kFrags; f += WK) {
     const int i = f / TMX, t = f % TMX;
-    v4f v = r4[f * 64 + lane];
-    for (int w = 1; w < WK; ++w) v += r4[(w * kFrags + f) * 64 + lane];
+    Acc va = r4[f * 64 + lane];
+    for (int w = 1; w < WK; ++w) va += r4[(w * kFrags + f) * 64 + lane];
     const int m = 16 * t + lr;
     if (m >= M) continue;
     const int n = n0 + 16 * i + 4 * g;
-    if (SPLIT > 1) {
-      *reinterpret_cast<v4f*>(ws + (static_cast<long>(s) * M + m) * N + n) = v;
+    if (SPLIT > 1) {  // raw partial (fp32, or int32 bits for the int8 engine)
+      *reinterpret_cast<Acc*>(ws + (static_cast<long>(s) * M + m) * N + n) = va;
       continue;
     }
+    v4f v = to_f32(va);
     if constexpr (!BLOCK) {
       const float sm = sa[m];
       const float4 s4 = *reinterpret_cast<const float4*>(sb + n);
@@ -503,8 +548,9 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
   }
 }
 
-// Ordered sum of the split-K partials, then (scaled_mm) the epilogue scales.
-template <bool BLOCK>
+// Ordered sum of the split-K partials (fp32, or exact int32 for the int8
+// engine), then (scaled_mm) the epilogue scales.
+template <bool BLOCK, bool INT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict__ y,
                                                             const float* __restrict__ ws,
                                                             const float* __restrict__ sa,
@@ -514,10 +560,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict
   for (long idx = blockIdx.x * 256L + threadIdx.x; idx < total; idx += gridDim.x * 256L) {
     const int m = static_cast<int>(idx / (N / 4));
     const int n = static_cast<int>(idx % (N / 4)) * 4;
-    float4 v = *reinterpret_cast<const float4*>(ws + static_cast<long>(m) * N + n);
-    for (int s = 1; s < SPLIT; ++s) {
-      const float4 u = *reinterpret_cast<const float4*>(ws + (static_cast<long>(s) * M + m) * N + n);
-      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    float4 v;
+    if constexpr (INT) {
+      int4 t = *reinterpret_cast<const int4*>(ws + static_cast<long>(m) * N + n);
+      for (int s = 1; s < SPLIT; ++s) {
+        const int4 u =
+            *reinterpret_cast<const int4*>(ws + (static_cast<long>(s) * M + m) * N + n);
+        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+      }
+      v = make_float4(static_cast<float>(t.x), static_cast<float>(t.y),
+                      static_cast<float>(t.z), static_cast<float>(t.w));
+    } else {
+      v = *reinterpret_cast<const float4*>(ws + static_cast<long>(m) * N + n);
+      for (int s = 1; s < SPLIT; ++s) {
+        const float4 u =
+            *reinterpret_cast<const float4*>(ws + (static_cast<long>(s) * M + m) * N + n);
+        v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+      }
     }
     if constexpr (!BLOCK) {
       const float sm = sa[m];
@@ -551,13 +610,14 @@ const char* keep_name(const std::string& n) {
 template <int BM, int BN, int WM, int WN, int ST, int E>
 Variant tiled_variant() {
   Variant v{};
-  const char* name = keep_name(std::string(E == kEngineF8 ? "f8" : "f16") + "_tiled_m" +
+  const char* name = keep_name(std::string(engine_prefix(E)) + "_tiled_m" +
                                std::to_string(BM) + "_n" + std::to_string(BN) + "_w" +
                                std::to_string(WM) + "x" + std::to_string(WN) + "_st" +
                                std::to_string(ST));
   v.cfg = GemmConfig{name, kTiled, E, BM, BN, WM, WN, 0, 0, 0, 1};
   v.fn[0] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, false, E>);
-  v.fn[1] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E>);
+  if constexpr (E != kEngineI8)
+    v.fn[1] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E>);
   v.threads = WM * WN * 64;
   v.lds = TiledShape<BM, BN, WM, WN, ST, true>::kLds;  // the larger of the two
   return v;
@@ -566,12 +626,13 @@ Variant tiled_variant() {
 template <int TMX, int RW, int WK, int J, int E>
 Variant skinny_variant() {
   Variant v{};
-  const char* name = keep_name(std::string(E == kEngineF8 ? "f8" : "f16") + "_skinny_t" +
+  const char* name = keep_name(std::string(engine_prefix(E)) + "_skinny_t" +
                                std::to_string(TMX) + "_r" + std::to_string(RW) + "_k" +
                                std::to_string(WK) + "_j" + std::to_string(J));
   v.cfg = GemmConfig{name, kSkinny, E, 0, 0, 0, 0, TMX, RW, WK, J};
   v.fn[0] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, J, false, E>);
-  v.fn[1] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, J, true, E>);
+  if constexpr (E != kEngineI8)
+    v.fn[1] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, J, true, E>);
   v.threads = WK * 64;
   v.lds = static_cast<size_t>(WK) * RW * TMX * 64 * 16;
   return v;
@@ -620,6 +681,29 @@ std::vector<Variant>& registry() {
     FP8Q_SKINNY(8, 1, 4, 4)
     FP8Q_SKINNY(8, 2, 4, 2)
 #undef FP8Q_SKINNY
+    // W8A8 INT8 (per-token x per-channel only)
+    v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineI8>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineI8>());
+    v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineI8>());
+    v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineI8>());
+#define FP8Q_SKINNY_I8(T, R, W, J) v.push_back(skinny_variant<T, R, W, J, kEngineI8>());
+    FP8Q_SKINNY_I8(1, 1, 4, 1)
+    FP8Q_SKINNY_I8(1, 1, 4, 4)
+    FP8Q_SKINNY_I8(1, 1, 4, 8)
+    FP8Q_SKINNY_I8(1, 2, 4, 4)
+    FP8Q_SKINNY_I8(1, 2, 4, 8)
+    FP8Q_SKINNY_I8(1, 4, 4, 4)
+    FP8Q_SKINNY_I8(1, 1, 8, 4)
+    FP8Q_SKINNY_I8(1, 2, 8, 4)
+    FP8Q_SKINNY_I8(2, 1, 4, 4)
+    FP8Q_SKINNY_I8(2, 2, 4, 4)
+    FP8Q_SKINNY_I8(4, 1, 4, 2)
+    FP8Q_SKINNY_I8(4, 1, 4, 4)
+    FP8Q_SKINNY_I8(4, 2, 4, 2)
+    FP8Q_SKINNY_I8(8, 1, 4, 2)
+    FP8Q_SKINNY_I8(8, 1, 4, 4)
+    FP8Q_SKINNY_I8(8, 2, 4, 2)
+#undef FP8Q_SKINNY_I8
     return v;
   }();
   return r;
@@ -672,6 +756,7 @@ hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, co
                        hipStream_t st) {
   const Variant& v = registry()[id];
   const int bw = blockwise ? 1 : 0;
+  if (v.fn[bw] == nullptr) return hipErrorInvalidDeviceFunction;
   ensure_lds_attr(v, bw);
   if (v.cfg.kind == kTiled) {
     const int tiles = (N / v.cfg.bn) * ((M + v.cfg.bm - 1) / v.cfg.bm);
@@ -691,11 +776,14 @@ hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, co
   long blocks = (total + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   if (blockwise)
-    hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(blocks), dim3(256), 0, st, y, wsf, sa,
-                       sb, M, N, split);
+    hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), dim3(blocks), dim3(256), 0, st, y,
+                       wsf, sa, sb, M, N, split);
+  else if (v.cfg.engine == kEngineI8)
+    hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), dim3(blocks), dim3(256), 0, st, y,
+                       wsf, sa, sb, M, N, split);
   else
-    hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(blocks), dim3(256), 0, st, y, wsf, sa,
-                       sb, M, N, split);
+    hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), dim3(blocks), dim3(256), 0, st, y,
+                       wsf, sa, sb, M, N, split);
   return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// Fused front end + dynamic FP8 (OCP e4m3) quantization kernels for gfx950.
+// Fused front end + dynamic FP8 (OCP e4m3) or INT8 quantization kernels for
+// gfx950.
 //
 // One kernel template covers the quantizers named on the page "Helion in
 // vLLM: FP8 inference of Qwen3" (24-ai.news), section "Kernels integrated
@@ -98,7 +99,13 @@ __device__ __forceinline__ float unit_max(float v, float* red) {
 // workgroup (TPR = 128 / 256: long rows, or few rows; cross-wave reductions
 // go through LDS).  Thread t of a unit owns the 8-element chunks t, t + TPR,
 // ..., CH of them.
-template <int OP, int MODE, int TPR, int CH>
+template <int FMT>
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+  if constexpr (FMT == kFmtI8) return pack4_i8(a, b, c, d);
+  return pack4_e4m3(a, b, c, d);
+}
+
+template <int OP, int MODE, int TPR, int CH, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q,
                                                          float* __restrict__ scale,
                                                          const uint16_t* __restrict__ x,
@@ -196,16 +203,18 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
 #pragma unroll
       for (int i = 1; i < CH; ++i) m = fmaxf(m, cmax[i]);
       const float amax = unit_max<TPR>(m, red32);
-      const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
+      const GroupScale g = FMT == kFmtI8      ? make_scale_i8(amax)
+                           : mode_is_ue8(MODE) ? make_scale_ue8m0(amax)
+                                               : make_scale(amax);
       if (active && tid == 0) scale[row] = g.s;
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         if (!valid[i]) continue;
         const int c = c0 + tid + i * TPR;
         uint2 out;
-        out.x = pack4_e4m3(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
+        out.x = pack4<FMT>(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
                            quotient(y[i][3], g));
-        out.y = pack4_e4m3(quotient(y[i][4], g), quotient(y[i][5], g), quotient(y[i][6], g),
+        out.y = pack4<FMT>(quotient(y[i][4], g), quotient(y[i][5], g), quotient(y[i][6], g),
                            quotient(y[i][7], g));
         *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
       }
@@ -219,9 +228,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
         const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
         if ((tid & 15) == 0) scale[static_cast<long>(row) * ngroups + c / 16] = g.s;
         uint2 out;
-        out.x = pack4_e4m3(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
+        out.x = pack4<FMT>(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
                            quotient(y[i][3], g));
-        out.y = pack4_e4m3(quotient(y[i][4], g), quotient(y[i][5], g), quotient(y[i][6], g),
+        out.y = pack4<FMT>(quotient(y[i][4], g), quotient(y[i][5], g), quotient(y[i][6], g),
                            quotient(y[i][7], g));
         *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
       }
@@ -232,9 +241,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
         if (!valid[i]) continue;
         const int c = c0 + tid + i * TPR;
         uint2 out;
-        out.x = pack4_e4m3(quotient_static(y[i][0], g), quotient_static(y[i][1], g),
+        out.x = pack4<FMT>(quotient_static(y[i][0], g), quotient_static(y[i][1], g),
                            quotient_static(y[i][2], g), quotient_static(y[i][3], g));
-        out.y = pack4_e4m3(quotient_static(y[i][4], g), quotient_static(y[i][5], g),
+        out.y = pack4<FMT>(quotient_static(y[i][4], g), quotient_static(y[i][5], g),
                            quotient_static(y[i][6], g), quotient_static(y[i][7], g));
         *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
       }
@@ -269,63 +278,71 @@ __global__ __launch_bounds__(kThreads) void silu_kernel(float* __restrict__ y,
 
 constexpr size_t kSiluLds = 8192 * sizeof(float);
 
-template <int OP, int MODE, int TPR, int CH>
+template <int OP, int MODE, int TPR, int CH, int FMT>
 hipError_t launch_quant_t(uint8_t* q, float* scale, const uint16_t* x, const uint16_t* w,
                           int M, int K, float eps, int grid, hipStream_t st) {
   const size_t lds = (OP == kSilu) ? kSiluLds : 0;
-  hipLaunchKernelGGL((quant_kernel<OP, MODE, TPR, CH>), dim3(grid), dim3(kThreads), lds, st, q,
+  hipLaunchKernelGGL((quant_kernel<OP, MODE, TPR, CH, FMT>), dim3(grid), dim3(kThreads), lds, st, q,
                      scale, x, w, M, K, eps);
   return hipGetLastError();
 }
 
-template <int OP, int MODE, int TPR>
+template <int OP, int MODE, int TPR, int FMT>
 hipError_t launch_quant_ch(int ch, uint8_t* q, float* scale, const uint16_t* x,
                            const uint16_t* w, int M, int K, float eps, int grid,
                            hipStream_t st) {
   switch (ch) {
-    case 1: return launch_quant_t<OP, MODE, TPR, 1>(q, scale, x, w, M, K, eps, grid, st);
-    case 2: return launch_quant_t<OP, MODE, TPR, 2>(q, scale, x, w, M, K, eps, grid, st);
-    case 4: return launch_quant_t<OP, MODE, TPR, 4>(q, scale, x, w, M, K, eps, grid, st);
-    case 6: return launch_quant_t<OP, MODE, TPR, 6>(q, scale, x, w, M, K, eps, grid, st);
-    case 8: return launch_quant_t<OP, MODE, TPR, 8>(q, scale, x, w, M, K, eps, grid, st);
-    case 10: return launch_quant_t<OP, MODE, TPR, 10>(q, scale, x, w, M, K, eps, grid, st);
-    case 12: return launch_quant_t<OP, MODE, TPR, 12>(q, scale, x, w, M, K, eps, grid, st);
-    case 16: return launch_quant_t<OP, MODE, TPR, 16>(q, scale, x, w, M, K, eps, grid, st);
+    case 1: return launch_quant_t<OP, MODE, TPR, 1, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 2: return launch_quant_t<OP, MODE, TPR, 2, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 4: return launch_quant_t<OP, MODE, TPR, 4, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 6: return launch_quant_t<OP, MODE, TPR, 6, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 8: return launch_quant_t<OP, MODE, TPR, 8, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 10: return launch_quant_t<OP, MODE, TPR, 10, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 12: return launch_quant_t<OP, MODE, TPR, 12, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 16: return launch_quant_t<OP, MODE, TPR, 16, FMT>(q, scale, x, w, M, K, eps, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Units of more than one wave only exist for whole-row units (per-token
 // modes and RMSNorm); other combinations instantiate the one-wave kernel only.
-template <int OP, int MODE>
+template <int OP, int MODE, int FMT>
 hipError_t launch_quant_tpr(int tpr, int ch, uint8_t* q, float* scale, const uint16_t* x,
                             const uint16_t* w, int M, int K, float eps, int grid,
                             hipStream_t st) {
   if (tpr == 64)
-    return launch_quant_ch<OP, MODE, 64>(ch, q, scale, x, w, M, K, eps, grid, st);
+    return launch_quant_ch<OP, MODE, 64, FMT>(ch, q, scale, x, w, M, K, eps, grid, st);
   if constexpr (mode_is_row(MODE) || OP == kRms) {
     if (tpr == 128)
-      return launch_quant_ch<OP, MODE, 128>(ch, q, scale, x, w, M, K, eps, grid, st);
-    return launch_quant_ch<OP, MODE, kThreads>(ch, q, scale, x, w, M, K, eps, grid, st);
+      return launch_quant_ch<OP, MODE, 128, FMT>(ch, q, scale, x, w, M, K, eps, grid, st);
+    return launch_quant_ch<OP, MODE, kThreads, FMT>(ch, q, scale, x, w, M, K, eps, grid, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <int OP>
+template <int OP, int FMT>
 hipError_t launch_quant_mode(int mode, int tpr, int ch, uint8_t* q, float* scale,
                              const uint16_t* x, const uint16_t* w, int M, int K, float eps,
                              int grid, hipStream_t st) {
+  if constexpr (FMT == kFmtI8) {
+    if (mode == kPerToken)
+      return launch_quant_tpr<OP, kPerToken, FMT>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    if (mode == kStaticTensor)
+      return launch_quant_tpr<OP, kStaticTensor, FMT>(tpr, ch, q, scale, x, w, M, K, eps, grid,
+                                                      st);
+    return hipErrorInvalidValue;
+  }
   switch (mode) {
     case kPerToken:
-      return launch_quant_tpr<OP, kPerToken>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+      return launch_quant_tpr<OP, kPerToken, FMT>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
     case kGroup128:
-      return launch_quant_tpr<OP, kGroup128>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+      return launch_quant_tpr<OP, kGroup128, FMT>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
     case kStaticTensor:
-      return launch_quant_tpr<OP, kStaticTensor>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+      return launch_quant_tpr<OP, kStaticTensor, FMT>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
     case kPerTokenUe8:
-      return launch_quant_tpr<OP, kPerTokenUe8>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+      return launch_quant_tpr<OP, kPerTokenUe8, FMT>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
     case kGroup128Ue8:
-      return launch_quant_tpr<OP, kGroup128Ue8>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+      return launch_quant_tpr<OP, kGroup128Ue8, FMT>(tpr, ch, q, scale, x, w, M, K, eps, grid, st);
     default:
       return hipErrorInvalidValue;
   }
@@ -342,9 +359,9 @@ int pick_ch(int chunks_per_thread) {
 
 int quant_max_k() { return kThreads * kChunk * 16; }
 
-hipError_t launch_quant(int op, int mode, uint8_t* q, float* scale, const uint16_t* x,
-                        const uint16_t* w, int M, int K, float eps, int num_cus,
-                        hipStream_t st) {
+hipError_t launch_quant(int op, int mode, int fmt, uint8_t* q, float* scale,
+                        const uint16_t* x, const uint16_t* w, int M, int K, float eps,
+                        int num_cus, hipStream_t st) {
   const bool whole_row = mode_is_row(mode) || (op == kRms);
   const int nchunk = K / kChunk;
   // Chunks a lane may hold before its registers cut occupancy too far (the
@@ -378,11 +395,20 @@ hipError_t launch_quant(int op, int mode, uint8_t* q, float* scale, const uint16
   // the SiLU table costs 32 KiB of LDS fill per workgroup: fewer, looping ones
   const long cap = static_cast<long>(num_cus) * (op == kSilu ? 4 : 16);
   const int grid = static_cast<int>(blocks < cap ? blocks : cap);
+  if (fmt == kFmtI8) {
+    if (op == kIdent)
+      return launch_quant_mode<kIdent, kFmtI8>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid,
+                                               st);
+    if (op == kRms)
+      return launch_quant_mode<kRms, kFmtI8>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    return launch_quant_mode<kSilu, kFmtI8>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+  }
   if (op == kIdent)
-    return launch_quant_mode<kIdent>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    return launch_quant_mode<kIdent, kFmtE4m3>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid,
+                                               st);
   if (op == kRms)
-    return launch_quant_mode<kRms>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
-  return launch_quant_mode<kSilu>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+    return launch_quant_mode<kRms, kFmtE4m3>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
+  return launch_quant_mode<kSilu, kFmtE4m3>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid, st);
 }
 
 hipError_t launch_cvt_e4m3(uint8_t* q, const float* x, long n, int num_cus, hipStream_t st) {

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_VERSION 101 /* major*100 + minor */
+#define FP8Q_VERSION 102 /* major*100 + minor */
 
 typedef enum {
   FP8Q_OK = 0,
@@ -81,7 +81,11 @@ typedef enum {
   FP8Q_GROUP128_UE8M0 = 4      /* one power-of-two scale per 1x128: [M, K/128]     (out) */
 } fp8q_quant_mode;
 
-typedef enum { FP8Q_OP_SCALED_MM = 0, FP8Q_OP_SCALED_MM_BLOCKWISE = 1 } fp8q_gemm_op;
+typedef enum {
+  FP8Q_OP_SCALED_MM = 0,
+  FP8Q_OP_SCALED_MM_BLOCKWISE = 1,
+  FP8Q_OP_SCALED_MM_INT8 = 2 /* W8A8 INT8, fp8q_scaled_mm_int8 */
+} fp8q_gemm_op;
 
 /* ------------------------------------------------------------------------
  * Fused RMSNorm + dynamic FP8 quantization
@@ -159,15 +163,45 @@ int fp8q_scaled_mm_blockwise(void* y, const void* a, const float* sa, const void
                              const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * W8A8 INT8: the same front ends and GEMM machinery with symmetric int8
+ * operands (page "Helion can accelerate vLLM LLM inference on NVIDIA GPUs",
+ * aihirek.info, section "Autotuning picks the right variant": W8A8_INT8
+ * beside FP8_Dynamic and Block_FP8).
+ *
+ * Quantizers: as their FP8 counterparts with
+ *   scale = RN32(amax / 127), q = clamp(rne(RN32(y / scale)), -127, 127),
+ *   an all-zero row gets scale 0 and q = 0;
+ *   q is int8 [M, K] (or [M, D]); modes FP8Q_PER_TOKEN (scale [M], out) and
+ *   FP8Q_PER_TENSOR_STATIC (scale [1], in) only (else FP8Q_ERR_BAD_MODE).
+ * GEMM (per-token x per-channel, "NT"):
+ *   y[m,n] = bf16( sa[m] * sb[n] * sum_k a[m,k] * b[n,k] ),
+ *   a int8 [M, K], b int8 [N, K], sa [M], sb [N] fp32; the integer sum is
+ *   exact (int32, so K <= 131072); ws as for fp8q_scaled_mm with
+ *   op FP8Q_OP_SCALED_MM_INT8.  Needs K % 128 == 0, N % 128 == 0.
+ * ---------------------------------------------------------------------- */
+int fp8q_rmsnorm_quant_int8(void* q, float* scale, const void* x, const void* w, int64_t M,
+                            int64_t K, float eps, int mode, void* stream);
+int fp8q_silu_mul_quant_int8(void* q, float* scale, const void* gate_up, int64_t M,
+                             int64_t D, int mode, void* stream);
+int fp8q_quant_int8(void* q, float* scale, const void* x, int64_t M, int64_t K, int mode,
+                    void* stream);
+int fp8q_scaled_mm_int8(void* y, const void* a, const void* b, const float* sa,
+                        const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* Bytes of workspace the GEMM `op` needs for this shape with the table's
  * choice (0 when the chosen variant needs none).  Pure host function. */
 size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K);
 
 /* ------------------------------------------------------------------------
- * GEMM variants.  The same two GEMMs with the variant forced instead of
- * taken from the per-shape table; used by tests (every variant is checked)
- * and by the table's tuner.  cfg < 0 means "use the table".
- * Returns FP8Q_ERR_BAD_CONFIG when cfg is unknown or cannot run this shape.
+ * GEMM variants.  The same GEMMs with the variant forced instead of taken
+ * from the per-shape table; used by tests (every variant is checked) and by
+ * the table's tuner.  cfg < 0 means "use the table".  Variant names start
+ * with the engine: f16_ (exact, the default), f8_ (FP8 MFMA, faster, sums
+ * truncated by the hardware), i8_ (int8 op only).
+ * Returns FP8Q_ERR_BAD_CONFIG when cfg is unknown, cannot run this shape,
+ * or belongs to another op.
  * ---------------------------------------------------------------------- */
 int fp8q_gemm_num_configs(void);
 const char* fp8q_gemm_config_name(int cfg);
@@ -179,6 +213,9 @@ int fp8q_scaled_mm_cfg(void* y, const void* a, const void* b, const float* sa,
 int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const float* sa, const void* b,
                                  const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                                  size_t ws_bytes, int cfg, void* stream);
+int fp8q_scaled_mm_int8_cfg(void* y, const void* a, const void* b, const float* sa,
+                            const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                            size_t ws_bytes, int cfg, void* stream);
 
 /* ------------------------------------------------------------------------
  * Elementwise building blocks (also used to test the device arithmetic

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_version() == 101
+    assert L.fp8q_version() == 102
     for s in range(10):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"
@@ -111,6 +111,29 @@ def test_gemm_argument_checks():
     assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 4096, A, need - 1, sp, None) == WS
 
 
+def test_int8_argument_checks():
+    L = fq.lib()
+    assert L.fp8q_quant_int8(A, B, C, 4, 128, 1, None) == MODE        # group: not for int8
+    assert L.fp8q_quant_int8(A, B, C, 4, 128, 3, None) == MODE        # UE8M0: not for int8
+    assert L.fp8q_rmsnorm_quant_int8(A, B, C, D, 4, 100, 1e-6, 0, None) == SHAPE
+    assert L.fp8q_rmsnorm_quant_int8(A, B, C, D, 4, 256, 0.0, 0, None) == INVALID
+    assert L.fp8q_silu_mul_quant_int8(A, B, C + 2, 4, 128, 0, None) == ALIGN
+    mm8 = L.fp8q_scaled_mm_int8
+    assert mm8(A, B, C, D, E, 0, 256, 256, None, 0, None) == OK
+    assert mm8(A, B, C, D, E, 4, 256, 100, None, 0, None) == SHAPE
+    assert mm8(A, B, C, D, E, 4, 256, 131072 + 128, None, 0, None) == SHAPE  # int32 bound
+    # engines serve only their own op
+    n = L.fp8q_gemm_num_configs()
+    i8 = next(i for i in range(n) if fq.fp8q_gemm_config_name(i).startswith("i8_tiled"))
+    f16 = next(i for i in range(n) if fq.fp8q_gemm_config_name(i).startswith("f16_tiled"))
+    assert L.fp8q_scaled_mm_int8_cfg(A, B, C, D, E, 4, 256, 256, None, 0, f16, None) == CFG
+    assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 4, 256, 256, None, 0, i8, None) == CFG
+    assert L.fp8q_scaled_mm_blockwise_cfg(A, B, C, D, E, 4, 256, 256, None, 0, i8, None) == CFG
+    for M in (1, 16, 128, 512, 2048):
+        cfg = fq.fp8q_gemm_config_for(fq.OP_SCALED_MM_INT8, M, 4096, 2048)
+        assert fq.fp8q_gemm_config_name(cfg).startswith("i8_")
+
+
 def test_elementwise_argument_checks():
     L = fq.lib()
     assert L.fp8q_cvt_e4m3(A, B, 0, None) == OK
@@ -129,6 +152,8 @@ def test_valid_calls_report_no_device_without_gpu():
     assert L.fp8q_scaled_mm_blockwise(A, B, C, D, E, 4, 256, 256, None, 0, None) == NODEV
     assert L.fp8q_cvt_e4m3(A, B, 16, None) == NODEV
     assert L.fp8q_silu(A, B, 16, None) == NODEV
+    assert L.fp8q_quant_int8(A, B, C, 4, 128, 0, None) == NODEV
+    assert L.fp8q_scaled_mm_int8(A, B, C, D, E, 4, 256, 256, None, 0, None) == NODEV
 
 
 def test_dispatch_table_covers_every_workload_shape():
