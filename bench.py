@@ -28,7 +28,8 @@ largest share of step time), timed with HIP events on its launch stream
 during the timed steps.  The CPU baseline runs the oracle on a bounded
 sample of that kernel's workload.  After the timed region, decode_chain
 reports the Qwen3-8B decode layer's 8-launch chain per M, launched eagerly
-and replayed from a HIP graph.
+and replayed from a HIP graph, and w8a8_int8 the int8 GEMMs on the
+Qwen3-1.7B shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -49,6 +50,7 @@ if ROOT not in sys.path:
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 F16_PEAK_TFLOPS = 2500.0      # MI355X dense f16/bf16 MFMA
+INT8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA
 HBM_PEAK_GBS = 8000.0
 
 PER_TOKEN, GROUP128 = 0, 1
@@ -413,6 +415,62 @@ def decode_chain_latency(step: Step, Ms=(1, 8, 32), reps: int = 50):
     return out
 
 
+def int8_sweep(step: Step, reps: int = 20):
+    """W8A8 INT8 on the Qwen3-1.7B per-token linear shapes: every GEMM shape
+    per M, back-to-back launches between two events (weights rotated over 8
+    copies), and the int8 RMSNorm quantizer.  Reported against the dense int8
+    MFMA peak (5.0 POP/s) and HBM."""
+    torch, L = step.torch, step.lib
+    hidden, (qkv_n, o_k, gu_n, inter), Ms = 2048, (4096, 2048, 12288, 6144), (1, 16, 128, 512,
+                                                                                2048)
+    shapes = [(qkv_n, hidden), (hidden, o_k), (gu_n, hidden), (hidden, inter)]
+    g = step.gen
+    out = {"workload": "qwen3-1.7b-per-token (int8)", "peak_tops": INT8_PEAK_TOPS, "per_M": {}}
+    tot_ops = tot_us = 0.0
+    st = step.stream
+    for M in Ms:
+        per = {}
+        for N, K in shapes:
+            a = torch.randint(-127, 128, (M, K), generator=g, device=step.dev, dtype=torch.int8)
+            bs = [torch.randint(-127, 128, (N, K), generator=g, device=step.dev,
+                                dtype=torch.int8) for _ in range(8)]
+            sa = torch.rand(M, generator=g, device=step.dev) * 1e-2
+            sb = torch.rand(N, generator=g, device=step.dev) * 1e-3
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=step.dev)
+            need = L.fp8q_workspace_size(2, M, N, K)
+            ws = torch.empty(((need + 3) // 4,), dtype=torch.float32, device=step.dev) if need \
+                else None
+            wsp = ws.data_ptr() if ws is not None else None
+
+            def run(i):
+                rc = L.fp8q_scaled_mm_int8(y.data_ptr(), a.data_ptr(), bs[i % 8].data_ptr(),
+                                           sa.data_ptr(), sb.data_ptr(), M, N, K, wsp, need, st)
+                if rc != 0:
+                    raise RuntimeError(f"int8 GEMM status {rc}")
+            for i in range(3):
+                run(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            ops = 2.0 * M * N * K
+            tot_ops += ops
+            tot_us += us
+            cfg = L.fp8q_gemm_config_for(2, M, N, K)
+            per[f"{N}x{K}"] = {"us": round(us, 2), "tops": round(ops / us / 1e6, 1),
+                               "gbs": round((M * K + N * K + 2 * M * N) / us / 1e3, 0),
+                               "variant": L.fp8q_gemm_config_name(cfg).decode()}
+        out["per_M"][f"M{M}"] = per
+    out["gemm_tops"] = round(tot_ops / tot_us / 1e6, 1)
+    big = out["per_M"]["M2048"][f"{gu_n}x{hidden}"]
+    out["largest_gemm_frac_of_int8_peak"] = round(big["tops"] / INT8_PEAK_TOPS, 4)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -487,6 +545,7 @@ def main():
               for wl, s in summary.items()}
 
     chain = decode_chain_latency(step)
+    w8a8 = int8_sweep(step)
 
     cpu = None
     if not args.no_cpu_baseline and dom[2] > 0:
@@ -516,6 +575,7 @@ def main():
         "cpu_baseline": cpu,
         "per_workload": per_wl,
         "decode_chain": chain,
+        "w8a8_int8": w8a8,
     }
     if args.detail:
         detail = {label: {"kind": kind, "us": round(kt[label], 2), "flops": flops,

@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 
 import fp8_block_scaled_rms_amd as fq  # noqa: E402
 
-MM, BW = fq.OP_SCALED_MM, fq.OP_SCALED_MM_BLOCKWISE
+MM, BW, I8 = fq.OP_SCALED_MM, fq.OP_SCALED_MM_BLOCKWISE, fq.OP_SCALED_MM_INT8
 
 # every GEMM of the Qwen3 FP8 workloads
 SHAPES = (
@@ -44,6 +44,9 @@ SHAPES = (
     + [(BW, M, N, K) for M in (2048, 8192)
        for N, K in ((10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600))]
     + [(BW, 64, 5120, 25600), (BW, 4096, 5120, 25600), (BW, 16, 512, 256)]
+    # W8A8 INT8 on the Qwen3-1.7B per-token shapes
+    + [(I8, M, N, K) for M in (1, 16, 128, 512, 2048)
+       for N, K in ((4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144))]
 )
 # M buckets between measured M values are served by the next larger one
 QUICK = [(BW, 8192, 51200, 5120), (BW, 2048, 10240, 5120), (BW, 32, 24576, 4096),
@@ -56,9 +59,11 @@ def variants(op, M, N, K, engine):
     out = []
     for i in range(fq.fp8q_gemm_num_configs()):
         name = fq.fp8q_gemm_config_name(i)
-        if engine == "exact" and not name.startswith("f16_"):
+        if (op == I8) != name.startswith("i8_"):  # engines serve their own op only
             continue
-        if engine == "fp8" and not name.startswith("f8_"):
+        if op != I8 and engine == "exact" and not name.startswith("f16_"):
+            continue
+        if op != I8 and engine == "fp8" and not name.startswith("f8_"):
             continue
         if "_skinny_" in name:
             tm = int(name.split("_skinny_t")[1].split("_")[0])
@@ -83,10 +88,15 @@ def time_shape(op, M, N, K, cands, reps=10):
     g.manual_seed(M * 7919 + N * 31 + K)
     wbytes = N * K
     copies = max(1, min(reps, (1 << 30) // max(wbytes, 1) + 1))
-    a = torch.randint(0, 255, (M, K), generator=g, device=dev, dtype=torch.uint8) & 0xF7
-    bs = [torch.randint(0, 255, (N, K), generator=g, device=dev, dtype=torch.uint8) & 0xF7
-          for _ in range(copies)]
-    if op == MM:
+    if op == I8:
+        a = torch.randint(-127, 128, (M, K), generator=g, device=dev, dtype=torch.int8)
+        bs = [torch.randint(-127, 128, (N, K), generator=g, device=dev, dtype=torch.int8)
+              for _ in range(copies)]
+    else:
+        a = torch.randint(0, 255, (M, K), generator=g, device=dev, dtype=torch.uint8) & 0xF7
+        bs = [torch.randint(0, 255, (N, K), generator=g, device=dev, dtype=torch.uint8) & 0xF7
+              for _ in range(copies)]
+    if op in (MM, I8):
         sa = torch.rand(M, generator=g, device=dev) + 0.5
         sb = torch.rand(N, generator=g, device=dev) + 0.5
     else:
@@ -101,6 +111,8 @@ def time_shape(op, M, N, K, cands, reps=10):
         def run(b):
             if op == MM:
                 fq.fp8q_scaled_mm(y, a, b, sa, sb, ws, cfg)
+            elif op == I8:
+                fq.fp8q_scaled_mm_int8(y, a, b, sa, sb, ws, cfg)
             else:
                 fq.fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws, cfg)
 
@@ -127,9 +139,9 @@ def write_table(rows, path):
     for op, M, N, K, name in rows:
         fam.setdefault((op, N, K), []).append((M, name))
     lines = ["// Per-shape GEMM variant table: {op, N, K, M_max, variant name}.",
-             "// op 0 = scaled_mm, 1 = scaled_mm_blockwise.  For a call (op, M, N, K) the",
-             "// first row with the same op, N and K and M <= M_max wins; shapes absent",
-             "// from the table use the built-in rule in dispatch.cpp.",
+             "// op 0 = scaled_mm, 1 = scaled_mm_blockwise, 2 = scaled_mm_int8.  For a call",
+             "// (op, M, N, K) the first row with the same op, N and K and M <= M_max wins;",
+             "// shapes absent from the table use the built-in rule in dispatch.cpp.",
              "// Written by fp8_block_scaled_rms_amd/tune.py from MI355X measurements."]
     for (op, N, K), ms in sorted(fam.items()):
         ms.sort()
@@ -144,7 +156,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default="tune_results.jsonl")
     ap.add_argument("--engine", default="exact", choices=["exact", "fp8", "all"])
-    ap.add_argument("--shapes", default="default", choices=["default", "quick", "large"])
+    ap.add_argument("--shapes", default="default", choices=["default", "quick", "large", "int8"])
     ap.add_argument("--write-table", default=None, help="path of the table to write")
     ap.add_argument("--reps", type=int, default=20)
     args = ap.parse_args()
@@ -154,7 +166,8 @@ def main():
             for line in f:
                 r = json.loads(line)
                 done[(r["op"], r["M"], r["N"], r["K"], r["variant"])] = r["us"]
-    shapes = {"default": SHAPES, "quick": QUICK, "large": LARGE}[args.shapes]
+    shapes = {"default": SHAPES, "quick": QUICK, "large": LARGE,
+              "int8": [sh for sh in SHAPES if sh[0] == I8]}[args.shapes]
     best_rows = []
     with open(args.out, "a") as f:
         for op, M, N, K in shapes:
@@ -171,7 +184,7 @@ def main():
             best = min(mine, key=mine.get)
             # the default table holds exact-engine variants only: the FP8-MFMA
             # engine's grouped truncation is outside the GEMM tolerance
-            exact = {n: us for n, us in mine.items() if n.startswith("f16_")}
+            exact = {n: us for n, us in mine.items() if n.startswith(("f16_", "i8_"))}
             best_exact = min(exact, key=exact.get) if exact else None
             flops = 2.0 * M * N * K
             byts = M * K + N * K + 2 * M * N
