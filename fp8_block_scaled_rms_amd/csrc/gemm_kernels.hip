@@ -287,7 +287,7 @@ __device__ __forceinline__ void wait_stage(int after) {
 // ST-stage ring of LDS buffers fed by direct global->LDS loads: the loads of
 // K block kb+ST-1 are in flight while block kb is multiplied, which covers
 // the HBM/L2 latency at the consumption rate of the matrix cores.
-template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E>
+template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E, int PRIO = 0>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     uint16_t* __restrict__ y, const uint8_t* __restrict__ A, const float* __restrict__ sa,
     const uint8_t* __restrict__ B, const float* __restrict__ sb, int M, int N, int K) {
@@ -388,6 +388,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     }
     // the buffer of block kb-1 is free: refill it with block kb+ST-1
     if (kb + ST - 1 < KB) load_stage(kb + ST - 1, (kb + ST - 1) % ST);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     Frag<E> xf[S::kFT];
 #pragma unroll
     for (int t = 0; t < S::kFT; ++t) xf[t] = prep<E>(xr[t]);
@@ -405,6 +406,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         }
       }
     }
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   }
 
   // epilogue: lane holds weight rows n..n+3 of token m
@@ -607,17 +609,19 @@ const char* keep_name(const std::string& n) {
   return names.back()->c_str();
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int E>
+template <int BM, int BN, int WM, int WN, int ST, int E, int PRIO = 0>
 Variant tiled_variant() {
   Variant v{};
   const char* name = keep_name(std::string(engine_prefix(E)) + "_tiled_m" +
                                std::to_string(BM) + "_n" + std::to_string(BN) + "_w" +
                                std::to_string(WM) + "x" + std::to_string(WN) + "_st" +
-                               std::to_string(ST));
+                               std::to_string(ST) + (PRIO ? "_p" : ""));
   v.cfg = GemmConfig{name, kTiled, E, BM, BN, WM, WN, 0, 0, 0, 1};
-  v.fn[0] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, false, E>);
+  v.fn[0] =
+      reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, false, E, PRIO>);
   if constexpr (E != kEngineI8)
-    v.fn[1] = reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E>);
+    v.fn[1] =
+        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E, PRIO>);
   v.threads = WM * WN * 64;
   v.lds = TiledShape<BM, BN, WM, WN, ST, true>::kLds;  // the larger of the two
   return v;
@@ -647,6 +651,8 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF16>());
     v.push_back(tiled_variant<256, 128, 4, 2, 3, kEngineF16>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 1>());
+    v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF16, 1>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF8>());
     v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineF8>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF8>());
