@@ -8,9 +8,9 @@
 namespace fp8q {
 
 // One compiled GEMM variant.
-//   kind kTiled:  LDS-staged, double-buffered tiles of bn weight rows x bm
-//                 tokens, wn x wm waves; every operand byte is read from HBM
-//                 once per tile row/column.
+//   kind kTiled:  LDS-staged tiles of bn weight rows x bm tokens in an
+//                 ST-stage ring, wn x wm waves; optionally split along K
+//                 (`split` workgroup rows, partials reduced in order).
 //   kind kSkinny: weight-streaming kernel for small M: a workgroup owns
 //                 rw*16 weight rows and all (<= tm*16) tokens; each of its wk
 //                 waves loads `split` (= j) K blocks at once; the waves are
@@ -32,7 +32,7 @@ struct GemmConfig {
   int engine;
   int bm, bn, wm, wn;  // kTiled
   int tm, rw, wk;      // kSkinny
-  int split;           // kSkinny: K blocks per wave (j)
+  int split;           // kSkinny: K blocks per wave (j); kTiled: split-K factor
 };
 
 int gemm_num_configs();

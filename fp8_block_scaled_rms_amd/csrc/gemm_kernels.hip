@@ -289,8 +289,9 @@ __device__ __forceinline__ void wait_stage(int after) {
 // the HBM/L2 latency at the consumption rate of the matrix cores.
 template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E, int PRIO = 0>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
-    uint16_t* __restrict__ y, const uint8_t* __restrict__ A, const float* __restrict__ sa,
-    const uint8_t* __restrict__ B, const float* __restrict__ sb, int M, int N, int K) {
+    uint16_t* __restrict__ y, float* __restrict__ ws, const uint8_t* __restrict__ A,
+    const float* __restrict__ sa, const uint8_t* __restrict__ B, const float* __restrict__ sb,
+    int M, int N, int K, int SPLIT) {
   using S = TiledShape<BM, BN, WM, WN, ST, BLOCK>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -304,6 +305,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   tile_coords(blockIdx.x, (M + BM - 1) / BM, N / BN, tn, tmi);
   const int n0 = tn * BN, m0 = tmi * BM;
   const int KB = K / kBK;
+  // split-K: workgroup row blockIdx.y takes K blocks [kb_first, kb_first + nkb)
+  const int per_split = (KB + SPLIT - 1) / SPLIT;
+  const int kb_first = static_cast<int>(blockIdx.y) * per_split;
+  const int nkb = (KB - kb_first < per_split) ? KB - kb_first : per_split;
 
   // per-thread, K-block-invariant parts of the load addresses
   uint32_t a_off[BM * 8 / S::kThreads], b_off[BN * 8 / S::kThreads];
@@ -360,14 +365,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 
 #pragma unroll
   for (int p = 0; p < ST - 1; ++p)
-    if (p < KB) load_stage(p, p);
+    if (p < nkb) load_stage(kb_first + p, p);
 
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb % ST;
-    const int after = (KB - 1 - kb < ST - 2) ? KB - 1 - kb : ST - 2;
+  for (int j = 0; j < nkb; ++j) {
+    const int buf = j % ST;
+    const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
     wait_stage<S::kLoadsPerStage, ST>(after);
-    // Block kb is in LDS (each wave waited for its own loads, whose data is
-    // written before the counter drops) and every wave is done reading kb-1.
+    // Block j is in LDS (each wave waited for its own loads, whose data is
+    // written before the counter drops) and every wave is done reading j-1.
     // A bare s_barrier: __syncthreads() would also wait for the loads of the
     // later stages still in flight.
     __builtin_amdgcn_s_barrier();
@@ -386,8 +391,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) sab[t] = sas[wm * S::kTM + 16 * t + lr] * sw;
     }
-    // the buffer of block kb-1 is free: refill it with block kb+ST-1
-    if (kb + ST - 1 < KB) load_stage(kb + ST - 1, (kb + ST - 1) % ST);
+    // the buffer of block j-1 is free: refill it with block j+ST-1
+    if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     Frag<E> xf[S::kFT];
 #pragma unroll
@@ -414,6 +419,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   for (int t = 0; t < S::kFT; ++t) {
     const int m = m0 + wm * S::kTM + 16 * t + lr;
     if (m >= M) continue;
+    if (SPLIT > 1) {  // raw partials (fp32, or int32 bits) for splitk_reduce_kernel
+#pragma unroll
+      for (int i = 0; i < S::kFW; ++i) {
+        const int n = n0 + wn * S::kTN + 16 * i + 4 * g;
+        *reinterpret_cast<typename AccT<E>::T*>(
+            ws + (static_cast<long>(blockIdx.y) * M + m) * N + n) = acc[i][t];
+      }
+      continue;
+    }
     float sm = 1.0f;
     if constexpr (!BLOCK) sm = sa[m];
 #pragma unroll
@@ -609,14 +623,18 @@ const char* keep_name(const std::string& n) {
   return names.back()->c_str();
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int E, int PRIO = 0>
+// SPLITK > 1: the K blocks are shared among SPLITK workgroup rows (fp32 or
+// int32 partials in the workspace, then splitk_reduce_kernel); a run-time
+// choice on the same kernel.
+template <int BM, int BN, int WM, int WN, int ST, int E, int PRIO = 0, int SPLITK = 1>
 Variant tiled_variant() {
   Variant v{};
   const char* name = keep_name(std::string(engine_prefix(E)) + "_tiled_m" +
                                std::to_string(BM) + "_n" + std::to_string(BN) + "_w" +
                                std::to_string(WM) + "x" + std::to_string(WN) + "_st" +
-                               std::to_string(ST) + (PRIO ? "_p" : ""));
-  v.cfg = GemmConfig{name, kTiled, E, BM, BN, WM, WN, 0, 0, 0, 1};
+                               std::to_string(ST) + (PRIO ? "_p" : "") +
+                               (SPLITK > 1 ? "_s" + std::to_string(SPLITK) : ""));
+  v.cfg = GemmConfig{name, kTiled, E, BM, BN, WM, WN, 0, 0, 0, SPLITK};
   v.fn[0] =
       reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, false, E, PRIO>);
   if constexpr (E != kEngineI8)
@@ -653,6 +671,11 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 1>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF16, 1>());
+    v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 4>());
+    v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 8>());
+    v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 16>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 0, 2>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 0, 4>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF8>());
     v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineF8>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF8>());
@@ -692,6 +715,8 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineI8>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineI8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineI8>());
+    v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineI8, 0, 4>());
+    v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineI8, 0, 2>());
 #define FP8Q_SKINNY_I8(T, R, W, J) v.push_back(skinny_variant<T, R, W, J, kEngineI8>());
     FP8Q_SKINNY_I8(1, 1, 4, 1)
     FP8Q_SKINNY_I8(1, 1, 4, 4)
@@ -749,10 +774,21 @@ int skinny_split(const GemmConfig& c, long K) {
   return static_cast<int>((kb + per - 1) / per);
 }
 
+// Workgroup rows along K for a tiled variant: c.split, reduced so that none
+// is empty.
+int tiled_split(const GemmConfig& c, long K) {
+  const long kb = K / kBK;
+  if (c.split <= 1 || kb <= 1) return 1;
+  const long per = (kb + c.split - 1) / c.split;
+  return static_cast<int>((kb + per - 1) / per);
+}
+
+int split_of(const GemmConfig& c, long K) {
+  return c.kind == kSkinny ? skinny_split(c, K) : tiled_split(c, K);
+}
+
 size_t gemm_workspace_bytes(int id, long M, long N, long K) {
-  const GemmConfig& c = gemm_config(id);
-  if (c.kind != kSkinny) return 0;
-  const int split = skinny_split(c, K);
+  const int split = split_of(gemm_config(id), K);
   if (split <= 1) return 0;
   return static_cast<size_t>(split) * M * N * sizeof(float);
 }
@@ -764,17 +800,14 @@ hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, co
   const int bw = blockwise ? 1 : 0;
   if (v.fn[bw] == nullptr) return hipErrorInvalidDeviceFunction;
   ensure_lds_attr(v, bw);
-  if (v.cfg.kind == kTiled) {
-    const int tiles = (N / v.cfg.bn) * ((M + v.cfg.bm - 1) / v.cfg.bm);
-    void* args[] = {&y, &a, &sa, &b, &sb, &M, &N, &K};
-    return hipLaunchKernel(v.fn[bw], dim3(tiles), dim3(v.threads), args, v.lds, st);
-  }
-  int split = skinny_split(v.cfg, K);
+  int split = split_of(v.cfg, K);
   float* wsf = static_cast<float*>(ws);
   {
     void* args[] = {&y, &wsf, &a, &sa, &b, &sb, &M, &N, &K, &split};
-    hipError_t e0 = hipLaunchKernel(v.fn[bw], dim3(N / (16 * v.cfg.rw), split), dim3(v.threads),
-                                    args, v.lds, st);
+    const dim3 grid = v.cfg.kind == kTiled
+                          ? dim3((N / v.cfg.bn) * ((M + v.cfg.bm - 1) / v.cfg.bm), split)
+                          : dim3(N / (16 * v.cfg.rw), split);
+    hipError_t e0 = hipLaunchKernel(v.fn[bw], grid, dim3(v.threads), args, v.lds, st);
     if (e0 != hipSuccess) return e0;
   }
   if (split <= 1) return hipSuccess;
