@@ -127,6 +127,50 @@ def _need(t: torch.Tensor, dtypes, what: str):
         raise ValueError(f"{what}: tensor must be contiguous")
 
 
+def _shape(t: torch.Tensor, shape, what: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _numel(t: torch.Tensor, n: int, what: str):
+    if t.numel() != n:
+        raise ValueError(f"{what}: {t.numel()} elements, expected {n}")
+
+
+def _one_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError(f"tensors must share one GPU device, got {sorted(map(str, devs))}")
+
+
+def _scale_numel(M: int, K: int, mode: int) -> int:
+    if mode in (PER_TOKEN, PER_TOKEN_UE8M0):
+        return M
+    if mode == PER_TENSOR_STATIC:
+        return 1
+    return M * (K // 128)
+
+
+def _check_quant(q, scale, x, M, K, mode, what, w=None):
+    """The caller's tensors must match the sizes passed to the library (the C
+    interface only sees pointers)."""
+    _shape(q, (M, K), f"{what}: q")
+    _numel(scale, _scale_numel(M, K, mode), f"{what}: scale")
+    if w is not None:
+        _shape(w, (K,), f"{what}: w")
+    _one_device(q, scale, x, w)
+
+
+def _check_gemm(y, a, b, sa, sb, ws, n_sa, n_sb, what):
+    M, K = a.shape
+    N = b.shape[0]
+    _shape(b, (N, K), f"{what}: b")
+    _shape(y, (M, N), f"{what}: y")
+    _numel(sa, n_sa, f"{what}: sa")
+    _numel(sb, n_sb, f"{what}: sb")
+    _one_device(y, a, b, sa, sb, ws)
+
+
 _E4M3 = (torch.uint8, torch.float8_e4m3fn)
 _I8 = (torch.int8,)
 _BF16 = (torch.bfloat16,)
@@ -138,6 +182,7 @@ _F32T = (torch.float32,)
 def fp8q_rmsnorm_quant(q, scale, x, w, eps: float, mode: int, stream=None) -> None:
     _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x"); _need(w, _BF16, "w")
     M, K = x.shape
+    _check_quant(q, scale, x, M, K, mode, "fp8q_rmsnorm_quant", w)
     _check(lib().fp8q_rmsnorm_quant(_ptr(q), _ptr(scale), _ptr(x), _ptr(w), M, K, eps, mode,
                                     _stream(stream)), "fp8q_rmsnorm_quant")
 
@@ -145,6 +190,9 @@ def fp8q_rmsnorm_quant(q, scale, x, w, eps: float, mode: int, stream=None) -> No
 def fp8q_silu_mul_quant(q, scale, gate_up, mode: int, stream=None) -> None:
     _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(gate_up, _BF16, "gate_up")
     M, twoD = gate_up.shape
+    if twoD % 2:
+        raise ValueError("fp8q_silu_mul_quant: gate_up needs an even number of columns")
+    _check_quant(q, scale, gate_up, M, twoD // 2, mode, "fp8q_silu_mul_quant")
     _check(lib().fp8q_silu_mul_quant(_ptr(q), _ptr(scale), _ptr(gate_up), M, twoD // 2, mode,
                                      _stream(stream)), "fp8q_silu_mul_quant")
 
@@ -152,6 +200,7 @@ def fp8q_silu_mul_quant(q, scale, gate_up, mode: int, stream=None) -> None:
 def fp8q_quant(q, scale, x, mode: int, stream=None) -> None:
     _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x")
     M, K = x.shape
+    _check_quant(q, scale, x, M, K, mode, "fp8q_quant")
     _check(lib().fp8q_quant(_ptr(q), _ptr(scale), _ptr(x), M, K, mode, _stream(stream)),
            "fp8q_quant")
 
@@ -161,6 +210,7 @@ def fp8q_scaled_mm(y, a, b, sa, sb, ws=None, cfg: int | None = None, stream=None
     _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
     M, K = a.shape
     N = b.shape[0]
+    _check_gemm(y, a, b, sa, sb, ws, M, N, "fp8q_scaled_mm")
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     if cfg is None:
         rc = lib().fp8q_scaled_mm(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K,
@@ -177,6 +227,8 @@ def fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws=None, cfg: int | None = None,
     _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
     M, K = a.shape
     N = b.shape[0]
+    _check_gemm(y, a, b, sa, sb, ws, M * (K // 128), (N // 128) * (K // 128),
+                "fp8q_scaled_mm_blockwise")
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     if cfg is None:
         rc = lib().fp8q_scaled_mm_blockwise(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N,
@@ -190,6 +242,7 @@ def fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws=None, cfg: int | None = None,
 def fp8q_rmsnorm_quant_int8(q, scale, x, w, eps: float, mode: int, stream=None) -> None:
     _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x"); _need(w, _BF16, "w")
     M, K = x.shape
+    _check_quant(q, scale, x, M, K, mode, "fp8q_rmsnorm_quant_int8", w)
     _check(lib().fp8q_rmsnorm_quant_int8(_ptr(q), _ptr(scale), _ptr(x), _ptr(w), M, K, eps, mode,
                                          _stream(stream)), "fp8q_rmsnorm_quant_int8")
 
@@ -197,6 +250,9 @@ def fp8q_rmsnorm_quant_int8(q, scale, x, w, eps: float, mode: int, stream=None) 
 def fp8q_silu_mul_quant_int8(q, scale, gate_up, mode: int, stream=None) -> None:
     _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(gate_up, _BF16, "gate_up")
     M, twoD = gate_up.shape
+    if twoD % 2:
+        raise ValueError("fp8q_silu_mul_quant_int8: gate_up needs an even number of columns")
+    _check_quant(q, scale, gate_up, M, twoD // 2, mode, "fp8q_silu_mul_quant_int8")
     _check(lib().fp8q_silu_mul_quant_int8(_ptr(q), _ptr(scale), _ptr(gate_up), M, twoD // 2,
                                           mode, _stream(stream)), "fp8q_silu_mul_quant_int8")
 
@@ -204,6 +260,7 @@ def fp8q_silu_mul_quant_int8(q, scale, gate_up, mode: int, stream=None) -> None:
 def fp8q_quant_int8(q, scale, x, mode: int, stream=None) -> None:
     _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x")
     M, K = x.shape
+    _check_quant(q, scale, x, M, K, mode, "fp8q_quant_int8")
     _check(lib().fp8q_quant_int8(_ptr(q), _ptr(scale), _ptr(x), M, K, mode, _stream(stream)),
            "fp8q_quant_int8")
 
@@ -213,6 +270,7 @@ def fp8q_scaled_mm_int8(y, a, b, sa, sb, ws=None, cfg: int | None = None, stream
     _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
     M, K = a.shape
     N = b.shape[0]
+    _check_gemm(y, a, b, sa, sb, ws, M, N, "fp8q_scaled_mm_int8")
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     if cfg is None:
         rc = lib().fp8q_scaled_mm_int8(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K,
@@ -244,11 +302,15 @@ def fp8q_gemm_config_for(op: int, M: int, N: int, K: int) -> int:
 
 def fp8q_cvt_e4m3(q, x, stream=None) -> None:
     _need(q, _E4M3, "q"); _need(x, _F32T, "x")
+    _numel(q, x.numel(), "fp8q_cvt_e4m3: q")
+    _one_device(q, x)
     _check(lib().fp8q_cvt_e4m3(_ptr(q), _ptr(x), x.numel(), _stream(stream)), "fp8q_cvt_e4m3")
 
 
 def fp8q_silu(y, g, stream=None) -> None:
     _need(y, _F32T, "y"); _need(g, _BF16, "g")
+    _numel(y, g.numel(), "fp8q_silu: y")
+    _one_device(y, g)
     _check(lib().fp8q_silu(_ptr(y), _ptr(g), g.numel(), _stream(stream)), "fp8q_silu")
 
 

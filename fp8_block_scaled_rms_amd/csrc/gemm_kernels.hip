@@ -41,6 +41,7 @@
 #include <memory>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 namespace fp8q {
@@ -740,18 +741,22 @@ std::vector<Variant>& registry() {
   return r;
 }
 
-// Raise the dynamic-LDS limit of each kernel once (above 64 KiB needs it).
+// Raise the dynamic-LDS limit of each kernel once per device (above 64 KiB
+// needs it).  A failure is not remembered, so the next launch retries and
+// the launch itself reports the error.
 void ensure_lds_attr(const Variant& v, int blockwise) {
+  if (v.lds <= 64 * 1024) return;
   static std::mutex mu;
-  static std::vector<const void*> done;
+  static std::vector<std::pair<int, const void*>> done;
   const void* fn = v.fn[blockwise];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
   std::lock_guard<std::mutex> lock(mu);
-  for (const void* d : done)
-    if (d == fn) return;
-  if (v.lds > 64 * 1024)
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(v.lds));
-  done.push_back(fn);
+  for (const auto& d : done)
+    if (d.first == dev && d.second == fn) return;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(v.lds)) == hipSuccess)
+    done.emplace_back(dev, fn);
 }
 
 }  // namespace
