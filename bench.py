@@ -28,8 +28,8 @@ largest share of step time), timed with HIP events on its launch stream
 during the timed steps.  The CPU baseline runs the oracle on a bounded
 sample of that kernel's workload.  After the timed region, decode_chain
 reports the Qwen3-8B decode layer's 8-launch chain per M, launched eagerly
-and replayed from a HIP graph, and w8a8_int8 the int8 GEMMs on the
-Qwen3-1.7B shapes.
+and replayed from a HIP graph, w8a8_int8 the int8 GEMMs on the Qwen3-1.7B
+shapes, and ue8m0_blockwise the prefill GEMMs with power-of-two scales.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -415,6 +415,51 @@ def decode_chain_latency(step: Step, Ms=(1, 8, 32), reps: int = 50):
     return out
 
 
+def ue8m0_gemm(step: Step, reps: int = 6):
+    """Qwen3-32B prefill GEMMs with power-of-two (UE8M0) block scales: the
+    blockwise GEMM on its general path vs the UE8M0 entry point, which folds
+    the scales into the f16 widening (same operands, weights rotated over two
+    copies)."""
+    torch, L = step.torch, step.lib
+    g = step.gen
+    out = {}
+    for M, N, K in ((8192, 51200, 5120), (2048, 10240, 5120)):
+        a = torch.randint(0, 255, (M, K), generator=g, device=step.dev, dtype=torch.uint8) & 0xF7
+        bs = [torch.randint(0, 255, (N, K), generator=g, device=step.dev, dtype=torch.uint8) & 0xF7
+              for _ in range(2)]
+        sa = torch.exp2(torch.randint(-8, 1, (M, K // 128), generator=g, device=step.dev)
+                        .float())
+        sb = torch.exp2(torch.randint(-14, -5, (N // 128, K // 128), generator=g,
+                                      device=step.dev).float())
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=step.dev)
+        res = {}
+        for kind, fn, op in (("general_us", L.fp8q_scaled_mm_blockwise, BW),
+                             ("ue8m0_folded_us", L.fp8q_scaled_mm_blockwise_ue8m0, 3)):
+            need = L.fp8q_workspace_size(op, M, N, K)
+            ws = torch.empty(((need + 3) // 4,), dtype=torch.float32, device=step.dev) if need \
+                else None
+            wsp = ws.data_ptr() if ws is not None else None
+
+            def run(i):
+                rc = fn(y.data_ptr(), a.data_ptr(), sa.data_ptr(), bs[i % 2].data_ptr(),
+                        sb.data_ptr(), M, N, K, wsp, need, step.stream)
+                if rc != 0:
+                    raise RuntimeError(f"blockwise GEMM status {rc}")
+            run(0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            res[kind] = round(e0.elapsed_time(e1) * 1e3 / reps, 1)
+        res["ue8m0_tflops"] = round(2.0 * M * N * K / res["ue8m0_folded_us"] / 1e6, 1)
+        res["general_tflops"] = round(2.0 * M * N * K / res["general_us"] / 1e6, 1)
+        out[f"M{M}_N{N}_K{K}"] = res
+    return out
+
+
 def int8_sweep(step: Step, reps: int = 20):
     """W8A8 INT8 on the Qwen3-1.7B per-token linear shapes: every GEMM shape
     per M, back-to-back launches between two events (weights rotated over 8
@@ -546,6 +591,7 @@ def main():
 
     chain = decode_chain_latency(step)
     w8a8 = int8_sweep(step)
+    ue8 = ue8m0_gemm(step)
 
     cpu = None
     if not args.no_cpu_baseline and dom[2] > 0:
@@ -576,6 +622,7 @@ def main():
         "per_workload": per_wl,
         "decode_chain": chain,
         "w8a8_int8": w8a8,
+        "ue8m0_blockwise": ue8,
     }
     if args.detail:
         detail = {label: {"kind": kind, "us": round(kt[label], 2), "flops": flops,

@@ -31,6 +31,7 @@ GROUP128_UE8M0 = 4
 OP_SCALED_MM = 0
 OP_SCALED_MM_BLOCKWISE = 1
 OP_SCALED_MM_INT8 = 2
+OP_SCALED_MM_BLOCKWISE_UE8M0 = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8q.so")
@@ -68,6 +69,10 @@ SIGNATURES = {
     "fp8q_scaled_mm_int8": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "fp8q_scaled_mm_int8_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT,
                                        _P]),
+    "fp8q_scaled_mm_blockwise_ue8m0": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ,
+                                              _P]),
+    "fp8q_scaled_mm_blockwise_ue8m0_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P,
+                                                  _SZ, _INT, _P]),
     "fp8q_cvt_e4m3": (_INT, [_P, _P, _I64, _P]),
     "fp8q_silu": (_INT, [_P, _P, _I64, _P]),
     "fp8q_status_string": (ctypes.c_char_p, [_INT]),
@@ -239,6 +244,25 @@ def fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws=None, cfg: int | None = None,
     _check(rc, "fp8q_scaled_mm_blockwise")
 
 
+def fp8q_scaled_mm_blockwise_ue8m0(y, a, sa, b, sb, ws=None, cfg: int | None = None,
+                                   stream=None) -> None:
+    _need(y, _BF16, "y"); _need(a, _E4M3, "a"); _need(b, _E4M3, "b")
+    _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    _check_gemm(y, a, b, sa, sb, ws, M * (K // 128), (N // 128) * (K // 128),
+                "fp8q_scaled_mm_blockwise_ue8m0")
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    if cfg is None:
+        rc = lib().fp8q_scaled_mm_blockwise_ue8m0(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                                                  M, N, K, _ptr(ws), wsb, _stream(stream))
+    else:
+        rc = lib().fp8q_scaled_mm_blockwise_ue8m0_cfg(_ptr(y), _ptr(a), _ptr(sa), _ptr(b),
+                                                      _ptr(sb), M, N, K, _ptr(ws), wsb, cfg,
+                                                      _stream(stream))
+    _check(rc, "fp8q_scaled_mm_blockwise_ue8m0")
+
+
 def fp8q_rmsnorm_quant_int8(q, scale, x, w, eps: float, mode: int, stream=None) -> None:
     _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x"); _need(w, _BF16, "w")
     M, K = x.shape
@@ -389,6 +413,14 @@ def quant_int8(x, mode: int, stream=None, scale=None):
     q, s = _int8_out(x.shape[0], x.shape[1], mode, scale, x.device)
     fp8q_quant_int8(q, s, x, mode, stream)
     return q, s
+
+
+def scaled_mm_blockwise_ue8m0(a, sa, b, sb, cfg: int | None = None, stream=None):
+    M, N = a.shape[0], b.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    ws = _workspace(OP_SCALED_MM_BLOCKWISE_UE8M0, M, N, a.shape[1], a.device, cfg)
+    fp8q_scaled_mm_blockwise_ue8m0(y, a, sa, b, sb, ws, cfg, stream)
+    return y
 
 
 def scaled_mm_int8(a, b, sa, sb, cfg: int | None = None, stream=None):

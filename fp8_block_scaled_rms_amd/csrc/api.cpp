@@ -116,8 +116,11 @@ int run_gemm(int op, void* y, const void* a, const float* sa, const void* b, con
   int num_cus = 0;
   rc = device_check(&num_cus);
   if (rc != FP8Q_OK) return rc;
+  const int scales = op == FP8Q_OP_SCALED_MM_BLOCKWISE         ? fp8q::kScalesBlock
+                     : op == FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0 ? fp8q::kScalesBlockPow2
+                                                               : fp8q::kScalesPerToken;
   return launched(fp8q::launch_gemm(
-      cfg, op == FP8Q_OP_SCALED_MM_BLOCKWISE, static_cast<uint16_t*>(y),
+      cfg, scales, static_cast<uint16_t*>(y),
       static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb,
       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), ws,
       static_cast<hipStream_t>(stream)));
@@ -203,6 +206,20 @@ int fp8q_scaled_mm_blockwise(void* y, const void* a, const float* sa, const void
                   stream);
 }
 
+int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const float* sa, const void* b,
+                                   const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return run_gemm(FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0, y, a, sa, b, sb, M, N, K, ws, ws_bytes,
+                  -1, stream);
+}
+
+int fp8q_scaled_mm_blockwise_ue8m0_cfg(void* y, const void* a, const float* sa, const void* b,
+                                       const float* sb, int64_t M, int64_t N, int64_t K,
+                                       void* ws, size_t ws_bytes, int cfg, void* stream) {
+  return run_gemm(FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0, y, a, sa, b, sb, M, N, K, ws, ws_bytes,
+                  cfg, stream);
+}
+
 int fp8q_scaled_mm_cfg(void* y, const void* a, const void* b, const float* sa,
                        const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                        size_t ws_bytes, int cfg, void* stream) {
@@ -218,9 +235,7 @@ int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const float* sa, const 
 
 size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  if (op != FP8Q_OP_SCALED_MM && op != FP8Q_OP_SCALED_MM_BLOCKWISE &&
-      op != FP8Q_OP_SCALED_MM_INT8)
-    return 0;
+  if (op < FP8Q_OP_SCALED_MM || op > FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0) return 0;
   const int cfg = fp8q::dispatch_gemm(op, M, N, K);
   return cfg < 0 ? 0 : fp8q::gemm_workspace_bytes(cfg, M, N, K);
 }

@@ -70,12 +70,16 @@ int rule(int op, long M, long N, long K) {
 bool variant_serves(int id, int op) {
   if (id < 0 || id >= gemm_num_configs()) return false;
   const bool i8 = gemm_config(id).engine == kEngineInt8;
-  return op == kOpInt8 ? i8 : (op == kOpScaledMm || op == kOpBlockwise) && !i8;
+  return op == kOpInt8 ? i8
+                       : (op == kOpScaledMm || op == kOpBlockwise || op == kOpBlockwisePow2) && !i8;
 }
 
 int dispatch_gemm(int op, long M, long N, long K) {
+  // power-of-two blockwise scales run the blockwise variants (the table is
+  // measured with general scales)
+  const int table_op = op == kOpBlockwisePow2 ? kOpBlockwise : op;
   for (const TableRow* r = kTable; r->variant != nullptr; ++r) {
-    if (r->op == op && r->n == N && r->k == K && M <= r->m_max) {
+    if (r->op == table_op && r->n == N && r->k == K && M <= r->m_max) {
       const int id = find_variant(r->variant);
       if (id >= 0 && variant_serves(id, op) && gemm_config_fits(id, M, N, K)) return id;
       break;

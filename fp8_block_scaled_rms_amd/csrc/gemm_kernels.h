@@ -42,10 +42,16 @@ const GemmConfig& gemm_config(int id);
 bool gemm_config_fits(int id, long M, long N, long K);
 size_t gemm_workspace_bytes(int id, long M, long N, long K);
 
-// blockwise == false: per-token x per-channel scales (sa [M], sb [N]);
-// blockwise == true : sa [M, K/128], sb [N/128, K/128] (not for kEngineInt8).
+// Scale layouts of a launch:
+//   kScalesPerToken: per-token x per-channel (sa [M], sb [N]);
+//   kScalesBlock:    sa [M, K/128], sb [N/128, K/128] (not for kEngineInt8);
+//   kScalesBlockPow2: the same, expected to hold powers of two (UE8M0), which
+//                    the tiled exact-engine kernels fold into the widening
+//                    (other kernels, or scales that do not qualify, take the
+//                    kScalesBlock path).
 // The operand bytes are e4m3 codes, or int8 values for a kEngineInt8 variant.
-hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, const float* sa,
+enum GemmScales { kScalesPerToken = 0, kScalesBlock = 1, kScalesBlockPow2 = 2 };
+hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const float* sa,
                        const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
                        hipStream_t st);
 

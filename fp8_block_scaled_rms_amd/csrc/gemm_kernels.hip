@@ -41,6 +41,7 @@
 #include <memory>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -116,6 +117,19 @@ __device__ __forceinline__ v8h widen8(int lo, int hi) {
   return r;
 }
 
+// The same widening multiplied by a power of two `scale` (exact whenever the
+// result is representable in f16, which the caller guarantees).
+__device__ __forceinline__ v8h widen8_scaled(int lo, int hi, float scale) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, scale, false);
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, scale, true);
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, false);
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, true);
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 // A fragment prepared for an engine: the raw bytes (kEngineF8) or four f16
 // slabs (kEngineF16).
 template <int E>
@@ -146,6 +160,28 @@ __device__ __forceinline__ Frag<E> prep(const v8i& raw) {
     for (int s = 0; s < 4; ++s) f.h[s] = widen8(raw[2 * s], raw[2 * s + 1]);
   }
   return f;
+}
+
+// prep<E> with the widened values multiplied by a power of two (exact f16
+// engine only; the other engines never fold scales and ignore `scale`).
+template <int E>
+__device__ __forceinline__ Frag<E> prep_scaled(const v8i& raw, float scale) {
+  if constexpr (E == kEngineF16) {
+    Frag<E> f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.h[s] = widen8_scaled(raw[2 * s], raw[2 * s + 1], scale);
+    return f;
+  } else {
+    (void)scale;
+    return prep<E>(raw);
+  }
+}
+
+// 2^(biased exponent of the power of two `s` - eref) as a float, eref chosen
+// so that the result lies in [2^-15, 2^7].
+__device__ __forceinline__ float pow2_rebased(float s, int eref) {
+  const int e = static_cast<int>((__float_as_uint(s) >> 23) & 0xFFu);
+  return __uint_as_float(static_cast<uint32_t>(e - eref + 127) << 23);
 }
 
 // c + W_block * X_block^T for one tile (weights on the 16-row side).
@@ -288,7 +324,17 @@ __device__ __forceinline__ void wait_stage(int after) {
 // ST-stage ring of LDS buffers fed by direct global->LDS loads: the loads of
 // K block kb+ST-1 are in flight while block kb is multiplied, which covers
 // the HBM/L2 latency at the consumption rate of the matrix cores.
-template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E, int PRIO = 0>
+// P2 (blockwise, exact engine): when every scale a wave uses is a power of
+// two and the exponents of its token rows and of its weight block each span
+// at most 22 binades over the K range, the scales are folded exactly into
+// the f16 widening (2^(e - eref), eref = largest exponent - 7, so every
+// widened value stays exactly representable in f16) and the MFMAs
+// accumulate across K blocks directly: no per-block scale FMA.  The wave
+// multiplies by 2^(eref_a + eref_b) in the epilogue.  Waves whose scales do
+// not qualify run the per-block FMA path.  UE8M0 scales (the page "Helion
+// in vLLM: FP8 inference of Qwen3", section "Practical limits") qualify.
+template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E, int PRIO = 0,
+          bool P2 = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     uint16_t* __restrict__ y, float* __restrict__ ws, const uint8_t* __restrict__ A,
     const float* __restrict__ sa, const uint8_t* __restrict__ B, const float* __restrict__ sb,
@@ -358,6 +404,55 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   };
 
   static_assert(!(BLOCK && E == kEngineI8), "the int8 engine is per-token x per-channel only");
+  static_assert(!P2 || (BLOCK && E == kEngineF16), "scale folding: blockwise, exact engine");
+
+  // reference exponents for folded power-of-two scales (see above)
+  int ea_ref[S::kFT];
+  int eb_ref = 0;
+  bool fold = false;
+  if constexpr (P2) {
+    bool ok = true;
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) {
+      const int mr = m0 + wm * S::kTM + 16 * t + lr;
+      const long row = (mr < M) ? mr : M - 1;
+      int emax = 0, emin = 255;
+      for (int kb = kb_first + g; kb < kb_first + nkb; kb += 4) {  // 4 lanes share a row
+        const uint32_t u = __float_as_uint(sa[row * KB + kb]);
+        const int e = static_cast<int>((u >> 23) & 0xFFu);
+        ok = ok && (u & 0x807FFFFFu) == 0 && e != 0 && e != 255;
+        emax = e > emax ? e : emax;
+        emin = e < emin ? e : emin;
+      }
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        const int a = __shfl_xor(emax, o), b = __shfl_xor(emin, o);
+        emax = a > emax ? a : emax;
+        emin = b < emin ? b : emin;
+      }
+      ea_ref[t] = emax - 7;
+      ok = ok && emax - emin <= 22;
+    }
+    const long nb = (n0 + wn * S::kTN) / 128;
+    int fmax = 0, fmin = 255;
+    for (int kb = kb_first + lane; kb < kb_first + nkb; kb += 64) {
+      const uint32_t u = __float_as_uint(sb[nb * KB + kb]);
+      const int e = static_cast<int>((u >> 23) & 0xFFu);
+      ok = ok && (u & 0x807FFFFFu) == 0 && e != 0 && e != 255;
+      fmax = e > fmax ? e : fmax;
+      fmin = e < fmin ? e : fmin;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a = __shfl_xor(fmax, o), b = __shfl_xor(fmin, o);
+      fmax = a > fmax ? a : fmax;
+      fmin = b < fmin ? b : fmin;
+    }
+    eb_ref = fmax - 7;
+    ok = ok && fmax - fmin <= 22;
+    fold = __all(ok);
+  }
+
   typename AccT<E>::T acc[S::kFW][S::kFT];
 #pragma unroll
   for (int i = 0; i < S::kFW; ++i)
@@ -368,51 +463,84 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   for (int p = 0; p < ST - 1; ++p)
     if (p < nkb) load_stage(kb_first + p, p);
 
-  for (int j = 0; j < nkb; ++j) {
-    const int buf = j % ST;
-    const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
-    wait_stage<S::kLoadsPerStage, ST>(after);
-    // Block j is in LDS (each wave waited for its own loads, whose data is
-    // written before the counter drops) and every wave is done reading j-1.
-    // A bare s_barrier: __syncthreads() would also wait for the loads of the
-    // later stages still in flight.
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const uint8_t* xs = smem + buf * S::kStage;
-    const uint8_t* ws = xs + S::kXBytes;
-    v8i xr[S::kFT], wr[S::kFW];
+  auto k_loop = [&](auto fold_c) {
+    constexpr bool FOLD = decltype(fold_c)::value;
+    for (int j = 0; j < nkb; ++j) {
+      const int buf = j % ST;
+      const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
+      wait_stage<S::kLoadsPerStage, ST>(after);
+      // Block j is in LDS (each wave waited for its own loads, whose data is
+      // written before the counter drops) and every wave is done reading j-1.
+      // A bare s_barrier: __syncthreads() would also wait for the loads of the
+      // later stages still in flight.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const uint8_t* xs = smem + buf * S::kStage;
+      const uint8_t* ws = xs + S::kXBytes;
+      v8i xr[S::kFT], wr[S::kFW];
 #pragma unroll
-    for (int t = 0; t < S::kFT; ++t) xr[t] = load_frag_lds(xs, wm * S::kTM + 16 * t + lr, g);
+      for (int t = 0; t < S::kFT; ++t) xr[t] = load_frag_lds(xs, wm * S::kTM + 16 * t + lr, g);
 #pragma unroll
-    for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(ws, wn * S::kTN + 16 * i + lr, g);
-    float sab[S::kFT];
-    if constexpr (BLOCK) {
-      const float* sas = reinterpret_cast<const float*>(ws + S::kWBytes);
-      const float sw = sas[BM + (wn * S::kTN) / 128];
+      for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(ws, wn * S::kTN + 16 * i + lr, g);
+      float sab[S::kFT];
+      float sxf[S::kFT];
+      float swf = 1.0f;
+      if constexpr (BLOCK) {
+        const float* sas = reinterpret_cast<const float*>(ws + S::kWBytes);
+        const float sw = sas[BM + (wn * S::kTN) / 128];
+        if constexpr (FOLD) {
+          swf = pow2_rebased(sw, eb_ref);
 #pragma unroll
-      for (int t = 0; t < S::kFT; ++t) sab[t] = sas[wm * S::kTM + 16 * t + lr] * sw;
-    }
-    // the buffer of block j-1 is free: refill it with block j+ST-1
-    if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
-    Frag<E> xf[S::kFT];
-#pragma unroll
-    for (int t = 0; t < S::kFT; ++t) xf[t] = prep<E>(xr[t]);
-#pragma unroll
-    for (int i = 0; i < S::kFW; ++i) {
-      const Frag<E> wf = prep<E>(wr[i]);
-#pragma unroll
-      for (int t = 0; t < S::kFT; ++t) {
-        if constexpr (BLOCK) {
-          const v4f p = block_mma<E>(wf, xf[t], acc_zero<E>());
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
+          for (int t = 0; t < S::kFT; ++t)
+            sxf[t] = pow2_rebased(sas[wm * S::kTM + 16 * t + lr], ea_ref[t]);
         } else {
-          acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
+#pragma unroll
+          for (int t = 0; t < S::kFT; ++t) sab[t] = sas[wm * S::kTM + 16 * t + lr] * sw;
         }
       }
+      // the buffer of block j-1 is free: refill it with block j+ST-1
+      if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+      Frag<E> xf[S::kFT];
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) {
+        if constexpr (FOLD)
+          xf[t] = prep_scaled<E>(xr[t], sxf[t]);
+        else
+          xf[t] = prep<E>(xr[t]);
+      }
+#pragma unroll
+      for (int i = 0; i < S::kFW; ++i) {
+        Frag<E> wf;
+        if constexpr (FOLD)
+          wf = prep_scaled<E>(wr[i], swf);
+        else
+          wf = prep<E>(wr[i]);
+#pragma unroll
+        for (int t = 0; t < S::kFT; ++t) {
+          if constexpr (BLOCK) {
+            if constexpr (!FOLD) {
+              const v4f p = block_mma<E>(wf, xf[t], acc_zero<E>());
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
+            } else {  // scales already folded into the operands
+              acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
+            }
+          } else {
+            acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
+          }
+        }
+      }
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  if constexpr (P2) {
+    if (fold)
+      k_loop(std::true_type{});
+    else
+      k_loop(std::false_type{});
+  } else {
+    k_loop(std::false_type{});
   }
 
   // epilogue: lane holds weight rows n..n+3 of token m
@@ -420,6 +548,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   for (int t = 0; t < S::kFT; ++t) {
     const int m = m0 + wm * S::kTM + 16 * t + lr;
     if (m >= M) continue;
+    if constexpr (P2) {
+      if (fold) {  // undo the folding: exact power-of-two rescale
+        const int sh = ea_ref[t] + eb_ref - 254;
+#pragma unroll
+        for (int i = 0; i < S::kFW; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = ldexpf(acc[i][t][r], sh);
+      }
+    }
     if (SPLIT > 1) {  // raw partials (fp32, or int32 bits) for splitk_reduce_kernel
 #pragma unroll
       for (int i = 0; i < S::kFW; ++i) {
@@ -610,7 +747,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict
 // ------------------------------------------------------ registry --
 struct Variant {
   GemmConfig cfg;
-  const void* fn[2];  // [blockwise]
+  const void* fn[3];  // [scale kind]: per-token, blockwise, blockwise with power-of-two folding
   int threads;
   size_t lds;
 };
@@ -641,6 +778,11 @@ Variant tiled_variant() {
   if constexpr (E != kEngineI8)
     v.fn[1] =
         reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E, PRIO>);
+  if constexpr (E == kEngineF16)
+    v.fn[2] = reinterpret_cast<const void*>(
+        &gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E, PRIO, true>);
+  else
+    v.fn[2] = v.fn[1];
   v.threads = WM * WN * 64;
   v.lds = TiledShape<BM, BN, WM, WN, ST, true>::kLds;  // the larger of the two
   return v;
@@ -656,6 +798,7 @@ Variant skinny_variant() {
   v.fn[0] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, J, false, E>);
   if constexpr (E != kEngineI8)
     v.fn[1] = reinterpret_cast<const void*>(&gemm_skinny_kernel<TMX, RW, WK, J, true, E>);
+  v.fn[2] = v.fn[1];  // no scale folding in the weight-streaming kernel
   v.threads = WK * 64;
   v.lds = static_cast<size_t>(WK) * RW * TMX * 64 * 16;
   return v;
@@ -744,11 +887,11 @@ std::vector<Variant>& registry() {
 // Raise the dynamic-LDS limit of each kernel once per device (above 64 KiB
 // needs it).  A failure is not remembered, so the next launch retries and
 // the launch itself reports the error.
-void ensure_lds_attr(const Variant& v, int blockwise) {
+void ensure_lds_attr(const Variant& v, int scales) {
   if (v.lds <= 64 * 1024) return;
   static std::mutex mu;
   static std::vector<std::pair<int, const void*>> done;
-  const void* fn = v.fn[blockwise];
+  const void* fn = v.fn[scales];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return;
   std::lock_guard<std::mutex> lock(mu);
@@ -798,11 +941,12 @@ size_t gemm_workspace_bytes(int id, long M, long N, long K) {
   return static_cast<size_t>(split) * M * N * sizeof(float);
 }
 
-hipError_t launch_gemm(int id, bool blockwise, uint16_t* y, const uint8_t* a, const float* sa,
+hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const float* sa,
                        const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
                        hipStream_t st) {
   const Variant& v = registry()[id];
-  const int bw = blockwise ? 1 : 0;
+  const int bw = scales;
+  const bool blockwise = scales != kScalesPerToken;
   if (v.fn[bw] == nullptr) return hipErrorInvalidDeviceFunction;
   ensure_lds_attr(v, bw);
   int split = split_of(v.cfg, K);

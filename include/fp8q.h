@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_VERSION 102 /* major*100 + minor */
+#define FP8Q_VERSION 103 /* major*100 + minor */
 
 typedef enum {
   FP8Q_OK = 0,
@@ -84,7 +84,8 @@ typedef enum {
 typedef enum {
   FP8Q_OP_SCALED_MM = 0,
   FP8Q_OP_SCALED_MM_BLOCKWISE = 1,
-  FP8Q_OP_SCALED_MM_INT8 = 2 /* W8A8 INT8, fp8q_scaled_mm_int8 */
+  FP8Q_OP_SCALED_MM_INT8 = 2,          /* W8A8 INT8, fp8q_scaled_mm_int8 */
+  FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0 = 3 /* fp8q_scaled_mm_blockwise_ue8m0 */
 } fp8q_gemm_op;
 
 /* ------------------------------------------------------------------------
@@ -190,6 +191,21 @@ int fp8q_scaled_mm_int8(void* y, const void* a, const void* b, const float* sa,
                         const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * scaled_mm_blockwise for power-of-two (UE8M0) scales, e.g. activations from
+ * the FP8Q_GROUP128_UE8M0 quantizer and weights with power-of-two block
+ * scales.  Same arguments and result as fp8q_scaled_mm_blockwise.  The tiled
+ * kernels fold such scales exactly into the e4m3 -> f16 widening and drop
+ * the per-block scale multiply-add (page "Helion in vLLM: FP8 inference of
+ * Qwen3", section "Practical limits", on UE8M0 scales); wherever a scale is
+ * not a power of two, or the exponents of one token row or weight block
+ * span more than 22 binades, those kernels take the general path, so any
+ * scales give the fp8q_scaled_mm_blockwise result.
+ * ---------------------------------------------------------------------- */
+int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const float* sa, const void* b,
+                                   const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* Bytes of workspace the GEMM `op` needs for this shape with the table's
  * choice (0 when the chosen variant needs none).  Pure host function. */
 size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K);
@@ -216,6 +232,9 @@ int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const float* sa, const 
 int fp8q_scaled_mm_int8_cfg(void* y, const void* a, const void* b, const float* sa,
                             const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                             size_t ws_bytes, int cfg, void* stream);
+int fp8q_scaled_mm_blockwise_ue8m0_cfg(void* y, const void* a, const float* sa, const void* b,
+                                       const float* sb, int64_t M, int64_t N, int64_t K,
+                                       void* ws, size_t ws_bytes, int cfg, void* stream);
 
 /* ------------------------------------------------------------------------
  * Elementwise building blocks (also used to test the device arithmetic

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_version() == 102
+    assert L.fp8q_version() == 103
     for s in range(10):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"

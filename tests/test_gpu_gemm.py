@@ -252,3 +252,75 @@ def test_gemm_m_zero_is_noop():
     b = torch.zeros((256, 256), dtype=torch.uint8, device=DEV)
     y = fq.scaled_mm(a, b, torch.empty(0, device=DEV), torch.ones(256, device=DEV))
     assert y.shape == (0, 256)
+
+
+# ------------------------------------- power-of-two (UE8M0) blockwise scales
+
+def _ue8m0_weight_blocks(W):
+    """W fp32 [N,K] -> e4m3 codes and power-of-two scales per 128x128 block
+    (the oracle's quantizer with the UE8M0 scale rule)."""
+    N, K = W.shape
+    blocks = W.reshape(N // 128, 128, K // 128, 128).transpose(0, 2, 1, 3)
+    codes, scale = quant.quantize_vectors_ue8m0(blocks.reshape(N // 128, K // 128, 128 * 128))
+    codes = codes.reshape(N // 128, K // 128, 128, 128).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(codes.reshape(N, K)), scale
+
+
+def _run_ue8(a, sa, b, sb, cfg=None):
+    y = fq.scaled_mm_blockwise_ue8m0(u8_dev(a), f32_dev(sa), u8_dev(b), f32_dev(sb), cfg=cfg)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("cfg,name", [c for c in _configs() if c[1].startswith("f16_")],
+                         ids=[n for _, n in _configs() if n.startswith("f16_")])
+def test_ue8m0_every_variant_one_hot_exact(cfg, name):
+    """Power-of-two scales (the folded path of the tiled kernels) with one-hot
+    weights: every output is one scaled e4m3 value, exact in bf16."""
+    M, N, K = _m_for(name), 256, 3072
+    say("ue8m0 variant one-hot", name)
+    rng = synth.rng_for("ue8-onehot", name)
+    a = synth.gen_e4m3_codes(rng, (M, K))
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), rng.permutation(K)[:N]] = 0x38
+    sa, sb = _scales(rng, BW, M, N, K, pow2=True)
+    y = bf16_host_f64(_run_ue8(a, sa, b, sb, cfg))
+    assert np.array_equal(y, _ref(BW, a, sa, b, sb))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 2048, 5120), (200, 1024, 8192), (2048, 10240, 5120)])
+def test_ue8m0_realistic_against_oracle(M, N, K):
+    """UE8M0 activations from the GPU quantizer and power-of-two weight block
+    scales, in the table's launch configuration."""
+    say("ue8m0 realistic", M, N, K)
+    rng = synth.rng_for("ue8-real", M, N, K)
+    x = synth.gen_activations(rng, M, K)
+    qa, sa_t = fq.quant(bf16_dev(x), fq.GROUP128_UE8M0)
+    a, sa = host(qa), host(sa_t)
+    b, sb = _ue8m0_weight_blocks(synth.gen_linear_weight(rng, N, K))
+    y = _run_ue8(a, sa, b, sb)
+    rows = _sampled_rows(M, 64) if M > 64 else np.arange(M)
+    ref = gemm.scaled_mm_blockwise(a[rows], sa[rows], b, sb)
+    res = gemm.acceptance(bf16_host_f64(y[torch.from_numpy(rows).to(DEV)]), ref)
+    assert res["ok"], res
+
+
+def test_ue8m0_falls_back_on_general_or_spread_scales():
+    """Scales that are not powers of two take the general path (same bytes as
+    scaled_mm_blockwise); so do power-of-two scales whose exponents span more
+    than the f16 window, which must still match the oracle."""
+    M, N, K = 200, 256, 3072
+    cfg = next(i for i, n in _configs() if n == "f16_tiled_m128_n128_w2x2_st2")
+    rng = synth.rng_for("ue8-fallback")
+    a = synth.gen_e4m3_codes(rng, (M, K))
+    b = synth.gen_e4m3_codes(rng, (N, K))
+    sa, sb = _scales(rng, BW, M, N, K)  # general fp32 scales
+    y_ue8 = _run_ue8(a, sa, b, sb, cfg)
+    y_gen = _run(BW, a, sa, b, sb, cfg)
+    assert torch.equal(y_ue8, y_gen)
+    sa2 = np.exp2(rng.integers(-4, 4, (M, K // 128))).astype(np.float32)
+    sa2[::3, 5] = np.float32(2.0 ** -40)  # 36+ binades below the rest of those rows
+    sb2 = np.exp2(rng.integers(-4, 4, (N // 128, K // 128))).astype(np.float32)
+    y = bf16_host_f64(_run_ue8(a, sa2, b, sb2, cfg))
+    res = gemm.acceptance(y, _ref(BW, a, sa2, b, sb2))
+    assert res["ok"], res
