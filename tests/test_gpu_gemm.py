@@ -324,3 +324,26 @@ def test_ue8m0_falls_back_on_general_or_spread_scales():
     y = bf16_host_f64(_run_ue8(a, sa2, b, sb2, cfg))
     res = gemm.acceptance(y, _ref(BW, a, sa2, b, sb2))
     assert res["ok"], res
+
+
+def test_calls_on_a_side_stream_are_ordered_by_that_stream():
+    """The library enqueues on the stream it is given: a chain on a side
+    stream (quantizer -> GEMM) reads the quantizer's output in order, and the
+    result equals the same chain on the default stream."""
+    M, N, K = 96, 2048, 4096
+    rng = synth.rng_for("stream", M, N, K)
+    x = bf16_dev(synth.gen_activations(rng, M, K))
+    w = bf16_dev(synth.gen_rms_weight(rng, K))
+    b = u8_dev(synth.gen_e4m3_codes(rng, (N, K)))
+    sb = f32_dev(synth.gen_scales(rng, (N // 128, K // 128)))
+    q0, s0 = fq.rmsnorm_quant(x, w, 1e-6, fq.GROUP128)
+    y0 = fq.scaled_mm_blockwise(q0, s0, b, sb)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q1, s1 = fq.rmsnorm_quant(x, w, 1e-6, fq.GROUP128)
+        y1 = fq.scaled_mm_blockwise(q1, s1, b, sb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(q0, q1) and torch.equal(s0, s1) and torch.equal(y0, y1)
