@@ -463,75 +463,156 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   for (int p = 0; p < ST - 1; ++p)
     if (p < nkb) load_stage(kb_first + p, p);
 
-  auto k_loop = [&](auto fold_c) {
+  // the raw fragments and block scales of block j from its LDS buffer
+  auto read_block = [&](int j, v8i(&xr)[S::kFT], v8i(&wr)[S::kFW], float(&sar)[S::kFT],
+                        float& swr) {
+    const uint8_t* xs = smem + (j % ST) * S::kStage;
+    const uint8_t* wsm = xs + S::kXBytes;
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) xr[t] = load_frag_lds(xs, wm * S::kTM + 16 * t + lr, g);
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(wsm, wn * S::kTN + 16 * i + lr, g);
+    if constexpr (BLOCK) {
+      const float* sas = reinterpret_cast<const float*>(wsm + S::kWBytes);
+      swr = sas[BM + (wn * S::kTN) / 128];
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) sar[t] = sas[wm * S::kTM + 16 * t + lr];
+    }
+  };
+
+  // one block's products from its raw fragments and scales
+  auto multiply = [&](auto fold_c, const v8i(&xr)[S::kFT], const v8i(&wr)[S::kFW],
+                      const float(&sar)[S::kFT], float swr) {
     constexpr bool FOLD = decltype(fold_c)::value;
-    for (int j = 0; j < nkb; ++j) {
-      const int buf = j % ST;
-      const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
-      wait_stage<S::kLoadsPerStage, ST>(after);
-      // Block j is in LDS (each wave waited for its own loads, whose data is
-      // written before the counter drops) and every wave is done reading j-1.
-      // A bare s_barrier: __syncthreads() would also wait for the loads of the
-      // later stages still in flight.
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      const uint8_t* xs = smem + buf * S::kStage;
-      const uint8_t* ws = xs + S::kXBytes;
-      v8i xr[S::kFT], wr[S::kFW];
+    float sab[S::kFT];
+    float sxf[S::kFT];
+    float swf = 1.0f;
+    if constexpr (BLOCK) {
+      if constexpr (FOLD) {
+        swf = pow2_rebased(swr, eb_ref);
 #pragma unroll
-      for (int t = 0; t < S::kFT; ++t) xr[t] = load_frag_lds(xs, wm * S::kTM + 16 * t + lr, g);
+        for (int t = 0; t < S::kFT; ++t) sxf[t] = pow2_rebased(sar[t], ea_ref[t]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(ws, wn * S::kTN + 16 * i + lr, g);
-      float sab[S::kFT];
-      float sxf[S::kFT];
-      float swf = 1.0f;
-      if constexpr (BLOCK) {
-        const float* sas = reinterpret_cast<const float*>(ws + S::kWBytes);
-        const float sw = sas[BM + (wn * S::kTN) / 128];
-        if constexpr (FOLD) {
-          swf = pow2_rebased(sw, eb_ref);
-#pragma unroll
-          for (int t = 0; t < S::kFT; ++t)
-            sxf[t] = pow2_rebased(sas[wm * S::kTM + 16 * t + lr], ea_ref[t]);
-        } else {
-#pragma unroll
-          for (int t = 0; t < S::kFT; ++t) sab[t] = sas[wm * S::kTM + 16 * t + lr] * sw;
-        }
+        for (int t = 0; t < S::kFT; ++t) sab[t] = sar[t] * swr;
       }
-      // the buffer of block j-1 is free: refill it with block j+ST-1
-      if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
-      Frag<E> xf[S::kFT];
+    }
+    Frag<E> xf[S::kFT];
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) {
+      if constexpr (FOLD)
+        xf[t] = prep_scaled<E>(xr[t], sxf[t]);
+      else
+        xf[t] = prep<E>(xr[t]);
+    }
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i) {
+      Frag<E> wf;
+      if constexpr (FOLD)
+        wf = prep_scaled<E>(wr[i], swf);
+      else
+        wf = prep<E>(wr[i]);
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) {
-        if constexpr (FOLD)
-          xf[t] = prep_scaled<E>(xr[t], sxf[t]);
-        else
-          xf[t] = prep<E>(xr[t]);
-      }
+        if constexpr (BLOCK) {
+          if constexpr (!FOLD) {
+            const v4f p = block_mma<E>(wf, xf[t], acc_zero<E>());
 #pragma unroll
-      for (int i = 0; i < S::kFW; ++i) {
-        Frag<E> wf;
-        if constexpr (FOLD)
-          wf = prep_scaled<E>(wr[i], swf);
-        else
-          wf = prep<E>(wr[i]);
-#pragma unroll
-        for (int t = 0; t < S::kFT; ++t) {
-          if constexpr (BLOCK) {
-            if constexpr (!FOLD) {
-              const v4f p = block_mma<E>(wf, xf[t], acc_zero<E>());
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
-            } else {  // scales already folded into the operands
-              acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
-            }
-          } else {
+            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[r], sab[t], acc[i][t][r]);
+          } else {  // scales already folded into the operands
             acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
+          }
+        } else {
+          acc[i][t] = block_mma<E>(wf, xf[t], acc[i][t]);
+        }
+      }
+    }
+  };
+
+  // Blockwise scales on the exact engine, without folding: the substeps
+  // of a block are the outer loop (consecutive matrix instructions are
+  // independent) and the products of block j are scaled into the
+  // accumulators while block j+1's first substep is issued, when they are
+  // long finished, instead of waiting at the end of block j for the last
+  // instructions of each chain.  The same products are added to the
+  // accumulators in the same order as in the plain loop.  (Not used where
+  // it would exceed 256 VGPRs and halve the occupancy: in the folding
+  // kernels, whose folded loop shares the register budget, and in two-wave
+  // tiles, whose lanes hold twice the load addresses.)
+  constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
+  auto k_loop_rotated = [&]() {
+    v4f p[S::kFW][S::kFT];
+    float sprev[S::kFT];
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) sprev[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i)
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) p[i][t] = v4f{0, 0, 0, 0};
+    v8i xr[S::kFT], wr[S::kFW];
+    float sar[S::kFT], swr = 0.0f;
+    for (int j = 0; j < nkb; ++j) {
+      const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
+      wait_stage<S::kLoadsPerStage, ST>(after);
+      __builtin_amdgcn_s_barrier();  // as in the plain loop below
+      asm volatile("" ::: "memory");
+      read_block(j, xr, wr, sar, swr);
+      if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        v8h xh[S::kFT];
+#pragma unroll
+        for (int t = 0; t < S::kFT; ++t) xh[t] = widen8(xr[t][2 * s], xr[t][2 * s + 1]);
+#pragma unroll
+        for (int i = 0; i < S::kFW; ++i) {
+          const v8h wh = widen8(wr[i][2 * s], wr[i][2 * s + 1]);
+#pragma unroll
+          for (int t = 0; t < S::kFT; ++t) {
+            if (s == 0) {  // block j-1's products (zeros before the first block)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sprev[t], acc[i][t][r]);
+              p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], v4f{0, 0, 0, 0}, 0, 0, 0);
+            } else {
+              p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], p[i][t], 0, 0, 0);
+            }
           }
         }
       }
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) sprev[t] = sar[t] * swr;
       if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+    }
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i)
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sprev[t], acc[i][t][r]);
+  };
+
+  auto k_loop = [&](auto fold_c) {
+    if constexpr (kRotate && !decltype(fold_c)::value) {
+      k_loop_rotated();
+    } else {
+      for (int j = 0; j < nkb; ++j) {
+        const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
+        wait_stage<S::kLoadsPerStage, ST>(after);
+        // Block j is in LDS (each wave waited for its own loads, whose data
+        // is written before the counter drops) and every wave is done
+        // reading j-1.  A bare s_barrier: __syncthreads() would also wait
+        // for the loads of the later stages still in flight.
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        v8i xr[S::kFT], wr[S::kFW];
+        float sar[S::kFT], swr = 0.0f;
+        read_block(j, xr, wr, sar, swr);
+        // the buffer of block j-1 is free: refill it with block j+ST-1
+        if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+        multiply(fold_c, xr, wr, sar, swr);
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+      }
     }
   };
   if constexpr (P2) {

@@ -118,6 +118,26 @@ def test_every_variant_random(cfg, name, op):
     _check_engine(name, op, y, a, sa, b, sb)
 
 
+def _tiled_configs():
+    return [c for c in _configs() if "_tiled_" in c[1]]
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 512])
+@pytest.mark.parametrize("cfg,name", _tiled_configs(), ids=[n for _, n in _tiled_configs()])
+def test_every_tiled_variant_short_k(cfg, name, K):
+    """K of 1 to 4 blocks: fewer K blocks than pipeline stages (and, with
+    split-K, workgroup rows left without blocks)."""
+    M, N = 200, 256
+    for op in (MM, BW):
+        say("gemm tiled short K", name, op, M, N, K)
+        rng = synth.rng_for("short-k", name, op, M, N, K)
+        a = synth.gen_e4m3_codes(rng, (M, K))
+        b = synth.gen_e4m3_codes(rng, (N, K))
+        sa, sb = _scales(rng, op, M, N, K)
+        y = _run(op, a, sa, b, sb, cfg)
+        _check_engine(name, op, y, a, sa, b, sb)
+
+
 @pytest.mark.parametrize("op", [MM, BW], ids=["mm", "blockwise"])
 @pytest.mark.parametrize("cfg,name", _configs(), ids=[n for _, n in _configs()])
 def test_every_variant_one_hot_exact(cfg, name, op):
