@@ -321,11 +321,26 @@ def build(step: Step):
     return cfg_of
 
 
+def queue_ahead(torch, cycles: int):
+    """Queue a spin kernel of `cycles` GPU clock cycles: launches issued next
+    wait behind it, so the GPU then runs them without waiting for the host,
+    whose cost per call through the binding (about 10 us) exceeds the
+    duration of a small kernel.  Events around them then time the kernels,
+    not the host."""
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cycles)
+
+
 def per_kernel_times(step: Step, reps: int = 3):
-    """Event-timed duration of every launch (median over reps)."""
+    """Event-timed GPU duration of every launch (median over reps).  Each
+    timed pass is issued right behind an untimed one, which keeps the GPU
+    busy (its large GEMMs take milliseconds) while the host issues the timed
+    pass, so no launch of the timed pass waits for the host."""
     torch = step.torch
     times = {label: [] for label, *_ in step.calls}
     for _ in range(reps):
+        torch.cuda.synchronize()
+        step.run()
         evs = []
         for label, kind, flops, nbytes, call in step.calls:
             e0 = torch.cuda.Event(enable_timing=True)
@@ -374,9 +389,10 @@ def cpu_baseline(step: Step, label: str, rows: int):
 
 def decode_chain_latency(step: Step, Ms=(1, 8, 32), reps: int = 50):
     """The Qwen3-8B block-decode layer chain (8 launches) per M, launched
-    eagerly through the C ABI and replayed from a HIP graph: the time per
-    chain back to back (between two events on the current stream), and the
-    wall-clock latency of one chain from an idle GPU (issue, then
+    eagerly through the C ABI and replayed from a HIP graph: the GPU time per
+    chain back to back (between two events on the current stream, the chains
+    queued behind a spin kernel so that the GPU never waits for the host), and
+    the wall-clock latency of one chain from an idle GPU (issue, then
     synchronize; median of 20)."""
     from fp8_block_scaled_rms_amd.graph import LinearChain
 
@@ -396,7 +412,7 @@ def decode_chain_latency(step: Step, Ms=(1, 8, 32), reps: int = 50):
                 fn()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
+            queue_ahead(torch, 8_000_000)  # ~4 ms: longer than issuing the chains
             e0.record()
             for _ in range(reps):
                 fn()
@@ -462,8 +478,8 @@ def ue8m0_gemm(step: Step, reps: int = 6):
 
 def int8_sweep(step: Step, reps: int = 20):
     """W8A8 INT8 on the Qwen3-1.7B per-token linear shapes: every GEMM shape
-    per M, back-to-back launches between two events (weights rotated over 8
-    copies), and the int8 RMSNorm quantizer.  Reported against the dense int8
+    per M, back-to-back launches between two events (queued behind a spin
+    kernel; weights rotated over 8 copies).  Reported against the dense int8
     MFMA peak (5.0 POP/s) and HBM."""
     torch, L = step.torch, step.lib
     hidden, (qkv_n, o_k, gu_n, inter), Ms = 2048, (4096, 2048, 12288, 6144), (1, 16, 128, 512,
@@ -496,6 +512,7 @@ def int8_sweep(step: Step, reps: int = 20):
                 run(i)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            queue_ahead(torch, 4_000_000)  # ~2 ms: longer than issuing the launches
             e0.record()
             for i in range(reps):
                 run(i)

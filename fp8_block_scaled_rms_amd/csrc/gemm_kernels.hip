@@ -700,9 +700,14 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
   }
   const long sb_row = static_cast<long>(n0 / 128) * KB;
 
-  // issue every load of this wave first
+  // issue every load of this wave first.  The block scales are loaded
+  // unconditionally from clamped (valid) addresses and masked afterwards: a
+  // load whose value is consumed inside a divergent branch makes the
+  // compiler wait there for every load issued before it, which would turn
+  // the J blocks into J round trips to memory.
   v8i wr[J][RW], xr[J][TMX];
   float sab[J][TMX];
+  float sar[J][TMX], sbr[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int kb = kb0 + WK * j;
@@ -715,11 +720,21 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
       xr[j][t] = (on && xok[t]) ? load_frag_global(xrow[t] + kb * kBK)
                                 : v8i{0, 0, 0, 0, 0, 0, 0, 0};
     if constexpr (BLOCK) {
-      const float sw = on ? sb[sb_row + kb] : 0.0f;
+      const int kbc = on ? kb : KB - 1;
+      sbr[j] = sb[sb_row + kbc];
+#pragma unroll
+      for (int t = 0; t < TMX; ++t) {
+        const long m = xok[t] ? 16 * t + lr : 0;
+        sar[j][t] = sa[m * KB + kbc];
+      }
+    }
+  }
+  if constexpr (BLOCK) {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int t = 0; t < TMX; ++t)
-        sab[j][t] = (on && xok[t]) ? sa[static_cast<long>(16 * t + lr) * KB + kb] * sw : 0.0f;
-    }
+        sab[j][t] = (kb0 + WK * j < KB && xok[t]) ? sar[j][t] * sbr[j] : 0.0f;
   }
 
   static_assert(!(BLOCK && E == kEngineI8), "the int8 engine is per-token x per-channel only");

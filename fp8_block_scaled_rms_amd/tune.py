@@ -82,6 +82,11 @@ def variants(op, M, N, K, engine):
     return out
 
 
+# GPU clock cycles of the spin kernel that the timed launches queue behind
+# (a few milliseconds, longer than the host needs to issue them)
+QUEUE_AHEAD_CYCLES = 8_000_000
+
+
 def time_shape(op, M, N, K, cands, reps=10):
     dev = "cuda:0"
     g = torch.Generator(device=dev)
@@ -118,8 +123,12 @@ def time_shape(op, M, N, K, cands, reps=10):
 
         for w in range(2):
             run(bs[w % copies])
-        # back-to-back launches between two events: the per-launch event
-        # overhead (several microseconds) would otherwise swamp small kernels
+        # Back-to-back launches between two events, all queued behind a spin
+        # kernel: the GPU then runs them without waiting for the host, whose
+        # per-call cost through this binding (about 10 us) exceeds a small
+        # kernel's duration.  Per-launch events would add their own overhead.
+        torch.cuda.synchronize()
+        torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
