@@ -949,6 +949,13 @@ std::vector<Variant>& registry() {
     FP8Q_SKINNY(8, 1, 4, 2)
     FP8Q_SKINNY(8, 1, 4, 4)
     FP8Q_SKINNY(8, 2, 4, 2)
+    // the whole of a long K in one launch (no split-K reduction): 8 or 16
+    // waves with 6 to 12 blocks each
+    FP8Q_SKINNY(1, 1, 8, 6)
+    FP8Q_SKINNY(1, 1, 8, 12)
+    FP8Q_SKINNY(1, 2, 8, 6)
+    FP8Q_SKINNY(1, 1, 16, 6)
+    FP8Q_SKINNY(2, 1, 8, 6)
 #undef FP8Q_SKINNY
     // W8A8 INT8 (per-token x per-channel only)
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineI8>());
