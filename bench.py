@@ -64,6 +64,13 @@ WORKLOADS = {
 }
 MLP_TAIL = ("qwen3-32b-mlp-tail", (64, 4096), 25600, 5120)
 TINY = ("tiny-blockwise", 16, 256, 512)
+# Workloads whose gate_up projection and SiLU-and-mul quantization run as one
+# kernel (fp8q_scaled_mm_blockwise_silu_quant: group-128 mode, large M).
+FUSED_MLP = ("qwen3-32b-block-prefill",)
+# name and op id under which the fused kernel is reported and its traffic
+# recorded (it is not one of the table's variants)
+FUSED_VARIANT = "f16_tiled_m128_n256_w2x4_st3_silu_quant"
+SQ = 4
 
 
 def parse():
@@ -88,7 +95,8 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_32b_prefill_gate_up_m8192.md")
 KERNEL_SOURCES = ("fp8_block_scaled_rms_amd/csrc/gemm_kernels.hip",
                   "fp8_block_scaled_rms_amd/csrc/gemm_kernels.h",
-                  "fp8_block_scaled_rms_amd/csrc/fp8q_common.hpp")
+                  "fp8_block_scaled_rms_amd/csrc/fp8q_common.hpp",
+                  "fp8_block_scaled_rms_amd/csrc/silu_table.hpp")
 
 
 def kernel_source_hash():
@@ -252,6 +260,24 @@ class Step:
         self.keep += [a, sa, b, sb]
         return y, cfg
 
+    def add_gemm_silu(self, label, a, sa, b, sb):
+        """gate_up GEMM (b: gate rows then up rows) with SiLU-and-mul and
+        group-128 quantization in its epilogue."""
+        torch, L = self.torch, self.lib
+        M, K = a.shape
+        N = b.shape[0]
+        q = self.empty((M, N // 2), torch.uint8)
+        s = self.empty((M, N // 256), torch.float32)
+        nbytes = M * K + N * K + M * (N // 2) + sa.numel() * 4 + sb.numel() * 4 + s.numel() * 4
+        fn = L.fp8q_scaled_mm_blockwise_silu_quant
+        args = (q.data_ptr(), s.data_ptr(), a.data_ptr(), sa.data_ptr(), b.data_ptr(),
+                sb.data_ptr(), M, N, K, self.stream)
+        self.operands[label] = (a, sa, b, sb)
+        self.calls.append((label, "scaled_mm_blockwise_silu_quant", 2 * M * N * K, nbytes,
+                           lambda: self._check(fn(*args), label)))
+        self.keep += [a, sa, b, sb]
+        return q, s
+
     def finalize(self):
         if self._ws_need:
             self.ws = self.torch.empty(((self._ws_need + 3) // 4,), dtype=self.torch.float32,
@@ -295,9 +321,13 @@ def build(step: Step):
             cfg_of[f"{tag}/o_proj"] = c
             x2 = step.activations(M, hidden)
             q, s = step.add_rmsnorm(f"{tag}/rmsnorm_quant2", x2, rw, mode)
-            gu, c = step.add_gemm(f"{tag}/gate_up", op, q, s, *wgu)
-            cfg_of[f"{tag}/gate_up"] = c
-            q, s = step.add_silu(f"{tag}/silu_mul_quant", gu, mode)
+            if name in FUSED_MLP:
+                q, s = step.add_gemm_silu(f"{tag}/gate_up_silu_mul_quant", q, s, *wgu)
+                cfg_of[f"{tag}/gate_up_silu_mul_quant"] = FUSED_VARIANT
+            else:
+                gu, c = step.add_gemm(f"{tag}/gate_up", op, q, s, *wgu)
+                cfg_of[f"{tag}/gate_up"] = c
+                q, s = step.add_silu(f"{tag}/silu_mul_quant", gu, mode)
             _, c = step.add_gemm(f"{tag}/down", op, q, s, *wdn)
             cfg_of[f"{tag}/down"] = c
     name, Ms, D, hidden = MLP_TAIL
@@ -331,6 +361,14 @@ def queue_ahead(torch, cycles: int):
     torch.cuda._sleep(cycles)
 
 
+def variant_name(fq, cfg):
+    """A table variant's name from its id; the fused kernel's name as is."""
+    if cfg is None or isinstance(cfg, str):
+        return cfg
+    name = fq.fp8q_gemm_config_name(cfg)
+    return name.decode() if isinstance(name, bytes) else name
+
+
 def per_kernel_times(step: Step, reps: int = 3):
     """Event-timed GPU duration of every launch (median over reps).  Each
     timed pass is issued right behind an untimed one, which keeps the GPU
@@ -356,8 +394,9 @@ def per_kernel_times(step: Step, reps: int = 3):
 
 
 def cpu_baseline(step: Step, label: str, rows: int):
-    """The oracle (rmsnorm_quant + blockwise or per-token GEMM as the kernel
-    is) on the first `rows` tokens of the dominant kernel's workload."""
+    """The oracle computing what the dominant kernel computes (the blockwise
+    or per-token GEMM; for the fused kernel also the bf16 rounding and the
+    group-128 SiLU-and-mul quantization) on its first `rows` tokens."""
     import threadpoolctl
 
     from oracle import gemm as ogemm
@@ -367,7 +406,6 @@ def cpu_baseline(step: Step, label: str, rows: int):
     a, sa, b, sb = step.operands[label]
     K = a.shape[1]
     N = b.shape[0]
-    blockwise = entry[1] == "scaled_mm_blockwise"
     a_h = a[:rows].cpu().numpy()
     sa_h = sa[:rows].cpu().numpy()
     b_h = b.cpu().numpy()
@@ -375,16 +413,22 @@ def cpu_baseline(step: Step, label: str, rows: int):
     info = threadpoolctl.threadpool_info()
     blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
-    if blockwise:
-        ogemm.scaled_mm_blockwise(a_h, sa_h, b_h, sb_h)
-    else:
+    if entry[1] == "scaled_mm":
         ogemm.scaled_mm(a_h, b_h, sa_h, sb_h)
+        what = "fp64 dequantized matmul"
+    else:
+        y = ogemm.scaled_mm_blockwise(a_h, sa_h, b_h, sb_h)
+        what = "fp64 dequantized matmul"
+        if entry[1] == "scaled_mm_blockwise_silu_quant":
+            import synth
+            oquant.silu_mul_quant(synth.f32_to_bf16_bits(y.astype(np.float32)), oquant.GROUP128)
+            what += ", bf16 rounding, SiLU-and-mul group-128 quantization"
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"{label} ({entry[1]}), first {rows} of {a.shape[0]} tokens, "
-                      f"N={N}, K={K}: fp64 dequantized matmul, {dt:.1f} s"}
+                      f"N={N}, K={K}: {what}, {dt:.1f} s"}
 
 
 def decode_chain_latency(step: Step, Ms=(1, 8, 32), reps: int = 50):
@@ -571,15 +615,16 @@ def main():
     durs = [a.elapsed_time(b) * 1e-3 for a, b in zip(*timer[dominant])]  # seconds
     dom_avg = float(np.mean(durs))
     dom = next(c for c in step.calls if c[0] == dominant)
-    dom_cfg = cfg_of.get(dominant)
-    dom_cfg_name = fq.fp8q_gemm_config_name(dom_cfg) if dom_cfg is not None else None
+    dom_cfg_name = variant_name(fq, cfg_of.get(dominant))
     exact = dom_cfg_name is None or dom_cfg_name.startswith("f16_")
     if dom[2] > 0:
         achieved = dom[2] / dom_avg / 1e12
         peak = F16_PEAK_TFLOPS if exact else FP8_PEAK_TFLOPS
         a_t, _, b_t, _ = step.operands[dominant]
-        traffic = measured_traffic(dom_cfg_name, MM if dom[1] == "scaled_mm" else BW,
-                                   a_t.shape[0], b_t.shape[0], a_t.shape[1])
+        dom_op = {"scaled_mm": MM, "scaled_mm_blockwise": BW,
+                  "scaled_mm_blockwise_silu_quant": SQ}[dom[1]]
+        traffic = measured_traffic(dom_cfg_name, dom_op, a_t.shape[0], b_t.shape[0],
+                                   a_t.shape[1])
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "algorithmic_bytes": dom[3],
@@ -644,8 +689,7 @@ def main():
     if args.detail:
         detail = {label: {"kind": kind, "us": round(kt[label], 2), "flops": flops,
                           "bytes": nbytes,
-                          "variant": (fq.fp8q_gemm_config_name(cfg_of[label])
-                                      if label in cfg_of else None)}
+                          "variant": variant_name(fq, cfg_of.get(label))}
                   for label, kind, flops, nbytes, _ in step.calls}
         with open(args.detail, "w") as f:
             json.dump(detail, f, indent=1)

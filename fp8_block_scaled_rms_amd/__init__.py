@@ -73,6 +73,8 @@ SIGNATURES = {
                                               _P]),
     "fp8q_scaled_mm_blockwise_ue8m0_cfg": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P,
                                                   _SZ, _INT, _P]),
+    "fp8q_scaled_mm_blockwise_silu_quant": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                                                   _P]),
     "fp8q_cvt_e4m3": (_INT, [_P, _P, _I64, _P]),
     "fp8q_silu": (_INT, [_P, _P, _I64, _P]),
     "fp8q_status_string": (ctypes.c_char_p, [_INT]),
@@ -263,6 +265,25 @@ def fp8q_scaled_mm_blockwise_ue8m0(y, a, sa, b, sb, ws=None, cfg: int | None = N
     _check(rc, "fp8q_scaled_mm_blockwise_ue8m0")
 
 
+def fp8q_scaled_mm_blockwise_silu_quant(q, scale, a, sa, b, sb, stream=None) -> None:
+    _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(a, _E4M3, "a")
+    _need(b, _E4M3, "b"); _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    what = "fp8q_scaled_mm_blockwise_silu_quant"
+    if N % 2:
+        raise ValueError(f"{what}: b needs an even number of rows (gate rows, then up rows)")
+    _shape(b, (N, K), f"{what}: b")
+    _shape(q, (M, N // 2), f"{what}: q")
+    _numel(scale, M * (N // 2 // 128), f"{what}: scale")
+    _numel(sa, M * (K // 128), f"{what}: sa")
+    _numel(sb, (N // 128) * (K // 128), f"{what}: sb")
+    _one_device(q, scale, a, sa, b, sb)
+    _check(lib().fp8q_scaled_mm_blockwise_silu_quant(_ptr(q), _ptr(scale), _ptr(a), _ptr(sa),
+                                                     _ptr(b), _ptr(sb), M, N, K,
+                                                     _stream(stream)), what)
+
+
 def fp8q_rmsnorm_quant_int8(q, scale, x, w, eps: float, mode: int, stream=None) -> None:
     _need(q, _I8, "q"); _need(scale, _F32T, "scale"); _need(x, _BF16, "x"); _need(w, _BF16, "w")
     M, K = x.shape
@@ -412,6 +433,17 @@ def silu_mul_quant_int8(gate_up, mode: int, stream=None, scale=None):
 def quant_int8(x, mode: int, stream=None, scale=None):
     q, s = _int8_out(x.shape[0], x.shape[1], mode, scale, x.device)
     fp8q_quant_int8(q, s, x, mode, stream)
+    return q, s
+
+
+def scaled_mm_blockwise_silu_quant(a, sa, b, sb, stream=None):
+    """(q [M, N/2] e4m3, scale [M, N/256] fp32) of silu_mul_quant (group
+    128) applied to the blockwise product with the gate rows b[:N/2] and the
+    up rows b[N/2:], in one kernel."""
+    M, N = a.shape[0], b.shape[0]
+    q = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
+    s = torch.empty((M, N // 2 // 128), dtype=torch.float32, device=a.device)
+    fp8q_scaled_mm_blockwise_silu_quant(q, s, a, sa, b, sb, stream)
     return q, s
 
 

@@ -213,6 +213,23 @@ int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const float* sa, cons
                   -1, stream);
 }
 
+int fp8q_scaled_mm_blockwise_silu_quant(void* q, float* scale, const void* a, const float* sa,
+                                        const void* b, const float* sb, int64_t M, int64_t N,
+                                        int64_t K, void* stream) {
+  int rc = check_gemm_args(FP8Q_OP_SCALED_MM_BLOCKWISE, q, a, b, sa, sb, M, N, K);
+  if (rc != FP8Q_OK || M == 0) return rc;
+  if (!scale) return FP8Q_ERR_INVALID_ARG;
+  if (!aligned16(scale)) return FP8Q_ERR_ALIGNMENT;
+  if (N % 256 != 0) return FP8Q_ERR_UNSUPPORTED_SHAPE;  // N/2 whole 128-column groups
+  int num_cus = 0;
+  rc = device_check(&num_cus);
+  if (rc != FP8Q_OK) return rc;
+  return launched(fp8q::launch_gemm_silu_quant(
+      static_cast<uint8_t*>(q), scale, static_cast<const uint8_t*>(a), sa,
+      static_cast<const uint8_t*>(b), sb, static_cast<int>(M), static_cast<int>(N),
+      static_cast<int>(K), static_cast<hipStream_t>(stream)));
+}
+
 int fp8q_scaled_mm_blockwise_ue8m0_cfg(void* y, const void* a, const float* sa, const void* b,
                                        const float* sb, int64_t M, int64_t N, int64_t K,
                                        void* ws, size_t ws_bytes, int cfg, void* stream) {

@@ -55,4 +55,13 @@ hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const 
                        const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
                        hipStream_t st);
 
+// Blockwise GEMM (exact engine, 128x256 tiles) with SiLU-and-mul and
+// group-128 e4m3 quantization in its epilogue: b holds N = 2D weight rows,
+// the gate rows then the up rows; writes q [M, D] e4m3 and scale [M, D/128]
+// fp32, as silu_mul_quant (group 128) of the bf16 [M, 2D] product would.
+// Requires D % 128 == 0 and K % 128 == 0.
+hipError_t launch_gemm_silu_quant(uint8_t* q, float* scale, const uint8_t* a, const float* sa,
+                                  const uint8_t* b, const float* sb, int M, int N, int K,
+                                  hipStream_t st);
+
 }  // namespace fp8q

@@ -36,6 +36,7 @@
 //    across workgroups through an fp32 workspace and an ordered reduction
 //    (page above: split K when M or N is too small to fill the GPU).
 #include "fp8q_common.hpp"
+#include "silu_table.hpp"
 #include "gemm_kernels.h"
 
 #include <memory>
@@ -333,8 +334,17 @@ __device__ __forceinline__ void wait_stage(int after) {
 // multiplies by 2^(eref_a + eref_b) in the epilogue.  Waves whose scales do
 // not qualify run the per-block FMA path.  UE8M0 scales (the page "Helion
 // in vLLM: FP8 inference of Qwen3", section "Practical limits") qualify.
+// SQ (SiLU-and-mul + group quantization fused into the epilogue; blockwise,
+// exact engine, 128x256 tiles of 2x4 waves): B holds N = 2D rows, the gate
+// rows [0, D) then the up rows [D, 2D), and the output is the e4m3 codes
+// q [M, D] (through `y`) with fp32 scales [M, D/128] (through `ws`) that
+// silu_mul_quant would produce, in group-128 mode, from the bf16 result of
+// the plain kernel -- without writing that result.  Each wave's 64 weight
+// rows are 32 gate rows and the 32 matching up rows, so a lane holds the
+// gate and up values of the same output columns, and the 128 output columns
+// of a workgroup are one quantization group.
 template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E, int PRIO = 0,
-          bool P2 = false>
+          bool P2 = false, bool SQ = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     uint16_t* __restrict__ y, float* __restrict__ ws, const uint8_t* __restrict__ A,
     const float* __restrict__ sa, const uint8_t* __restrict__ B, const float* __restrict__ sb,
@@ -366,11 +376,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     const int row = (m0 + r < M) ? m0 + r : M - 1;
     a_off[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
   }
+  static_assert(!SQ || (BLOCK && E == kEngineF16 && !P2 && S::kTN == 64 && WN * 32 == 128),
+                "fused SiLU-and-mul quantization: blockwise exact engine, 128 output columns");
+  // SQ: LDS weight row r (wave r / 64) is gate row 32 (r / 64) + r % 64 of the
+  // output column tile, or the matching up row for r % 64 >= 32
+  const int D = N / 2;
+  const int o0 = tn * 128;  // SQ: first output column of the tile
+  auto b_row = [&](int r) -> int {
+    if constexpr (SQ) {
+      const int w = r >> 6, l = r & 63;
+      return (l < 32) ? o0 + 32 * w + l : D + o0 + 32 * w + (l - 32);
+    } else {
+      return n0 + r;
+    }
+  };
 #pragma unroll
   for (int j = 0; j < BN * 8 / S::kThreads; ++j) {
     const int qi = j * S::kThreads + tid;
     const int r = qi >> 3, p = qi & 7;
-    b_off[j] = static_cast<uint32_t>(n0 + r) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
+    b_off[j] = static_cast<uint32_t>(b_row(r)) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
   }
   // blockwise scales: wave w fetches floats [64w, 64w+64) of [sa column | sb | pad]
   const float* s_src = sa;
@@ -382,7 +406,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       s_off = static_cast<long>(row) * KB;
     } else if (q < BM + BN / 128) {
       s_src = sb;
-      s_off = static_cast<long>(n0 / 128 + (q - BM)) * KB;
+      const int blk = SQ ? (q == BM ? o0 / 128 : (D + o0) / 128) : n0 / 128 + (q - BM);
+      s_off = static_cast<long>(blk) * KB;
     } else {
       s_off = static_cast<long>(m0) * KB;  // padding: any valid address
     }
@@ -463,9 +488,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   for (int p = 0; p < ST - 1; ++p)
     if (p < nkb) load_stage(kb_first + p, p);
 
-  // the raw fragments and block scales of block j from its LDS buffer
+  // the raw fragments and block scales of block j from its LDS buffer (SQ:
+  // swr_hi is the up rows' weight scale, swr the gate rows'; else equal)
   auto read_block = [&](int j, v8i(&xr)[S::kFT], v8i(&wr)[S::kFW], float(&sar)[S::kFT],
-                        float& swr) {
+                        float& swr, float& swr_hi) {
     const uint8_t* xs = smem + (j % ST) * S::kStage;
     const uint8_t* wsm = xs + S::kXBytes;
 #pragma unroll
@@ -474,7 +500,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(wsm, wn * S::kTN + 16 * i + lr, g);
     if constexpr (BLOCK) {
       const float* sas = reinterpret_cast<const float*>(wsm + S::kWBytes);
-      swr = sas[BM + (wn * S::kTN) / 128];
+      if constexpr (SQ) {
+        swr = sas[BM];
+        swr_hi = sas[BM + 1];
+      } else {
+        swr = sas[BM + (wn * S::kTN) / 128];
+        swr_hi = swr;
+      }
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) sar[t] = sas[wm * S::kTM + 16 * t + lr];
     }
@@ -542,22 +574,38 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
   auto k_loop_rotated = [&]() {
     v4f p[S::kFW][S::kFT];
-    float sprev[S::kFT];
+    // block scales of the previous block per token, for the lower and (SQ:
+    // up rows) the upper half of the wave's weight fragments
+    float sprev[S::kFT], sprev_hi[S::kFT];
 #pragma unroll
-    for (int t = 0; t < S::kFT; ++t) sprev[t] = 0.0f;
+    for (int t = 0; t < S::kFT; ++t) sprev[t] = sprev_hi[t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < S::kFW; ++i)
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) p[i][t] = v4f{0, 0, 0, 0};
     v8i xr[S::kFT], wr[S::kFW];
-    float sar[S::kFT], swr = 0.0f;
+    float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
     for (int j = 0; j < nkb; ++j) {
       const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
       wait_stage<S::kLoadsPerStage, ST>(after);
       __builtin_amdgcn_s_barrier();  // as in the plain loop below
       asm volatile("" ::: "memory");
-      read_block(j, xr, wr, sar, swr);
+      read_block(j, xr, wr, sar, swr, swr_hi);
       if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
+      if constexpr (SQ) {
+        // SQ: the buffer after the last block's is free for good; the SiLU
+        // table (32 KiB: 4 x 1 KiB per wave) goes there while the last
+        // block is multiplied
+        if (j == nkb - 1) {
+          const uint32_t tl = lds0 + ((j + 1) % ST) * S::kStage;
+          const uint8_t* tg = reinterpret_cast<const uint8_t*>(kSiluTable);
+#pragma unroll
+          for (int c = 0; c < 32 / S::kWaves; ++c) {
+            const int chunk = wave * (32 / S::kWaves) + c;
+            g2lds16(tg + chunk * 1024 + lane * 16, tl + chunk * 1024);
+          }
+        }
+      }
       if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -570,8 +618,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
           for (int t = 0; t < S::kFT; ++t) {
             if (s == 0) {  // block j-1's products (zeros before the first block)
+              const float sp = (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sprev[t], acc[i][t][r]);
+              for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
               p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], v4f{0, 0, 0, 0}, 0, 0, 0);
             } else {
               p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], p[i][t], 0, 0, 0);
@@ -580,15 +629,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         }
       }
 #pragma unroll
-      for (int t = 0; t < S::kFT; ++t) sprev[t] = sar[t] * swr;
+      for (int t = 0; t < S::kFT; ++t) {
+        sprev[t] = sar[t] * swr;
+        sprev_hi[t] = sar[t] * swr_hi;
+      }
       if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 #pragma unroll
     for (int i = 0; i < S::kFW; ++i)
 #pragma unroll
-      for (int t = 0; t < S::kFT; ++t)
+      for (int t = 0; t < S::kFT; ++t) {
+        const float sp = (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sprev[t], acc[i][t][r]);
+        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
+      }
   };
 
   auto k_loop = [&](auto fold_c) {
@@ -605,8 +659,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         v8i xr[S::kFT], wr[S::kFW];
-        float sar[S::kFT], swr = 0.0f;
-        read_block(j, xr, wr, sar, swr);
+        float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
+        read_block(j, xr, wr, sar, swr, swr_hi);
         // the buffer of block j-1 is free: refill it with block j+ST-1
         if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
@@ -622,6 +676,71 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       k_loop(std::false_type{});
   } else {
     k_loop(std::false_type{});
+  }
+
+  if constexpr (SQ) {
+    // Fused epilogue.  Lane (lr, g) holds, for token lr of fragment t, the
+    // gate values of output columns 32 wn + 16 h + 4 g + r (fragments h = 0,
+    // 1) and the up values of the same columns (fragments h + 2).  Each is
+    // rounded to bf16 as the plain kernel stores it, then y = silu(gate) * up
+    // and the group-128 quantization follow silu_mul_quant exactly.
+    // The table was loaded into the buffer after the last block's (K loop
+    // above); once this wave's loads have landed and every wave is past the
+    // barrier, it is complete and no wave reads the staging buffers any more.
+    wait_vm<0>();
+    __syncthreads();
+    const int jl = nkb - 1;
+    const float* tab = reinterpret_cast<const float*>(smem + ((jl + 1) % ST) * S::kStage);
+    float* red = reinterpret_cast<float*>(smem + (jl % ST) * S::kStage);  // [BM][WN] amax
+    constexpr int kH = S::kFW / 2;
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    // round to bf16 (nearest even, as the plain kernel's stores) two values at a time
+    auto bf16x2 = [](float lo, float hi) -> uint32_t {
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf));
+    };
+    float v[S::kFT][kH][4];
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) {
+      float cm = 0.0f;
+#pragma unroll
+      for (int h = 0; h < kH; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const uint32_t gb = bf16x2(acc[h][t][r], acc[h][t][r + 1]);
+          const uint32_t ub = bf16x2(acc[h + kH][t][r], acc[h + kH][t][r + 1]);
+          v[t][h][r] = silu_bf16(gb & 0xFFFFu, tab) * __uint_as_float(ub << 16);
+          v[t][h][r + 1] = silu_bf16(gb >> 16, tab) * __uint_as_float(ub & 0xFFFF0000u);
+          cm = fmaxf(cm, fmaxf(fabsf(v[t][h][r]), fabsf(v[t][h][r + 1])));
+        }
+      // the wave's 32 columns of this token sit in lanes lr, lr + 16, lr + 32, lr + 48
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      if (g == 0) red[(wm * S::kTM + 16 * t + lr) * WN + wn] = cm;
+    }
+    __syncthreads();
+    uint8_t* q = reinterpret_cast<uint8_t*>(y);
+    const int ngroups = D / 128;
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) {
+      const int row = wm * S::kTM + 16 * t + lr;
+      const int m = m0 + row;
+      float amax = red[row * WN];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[row * WN + w]);
+      if (m >= M) continue;
+      const GroupScale gs = make_scale(amax);
+      if (wn == 0 && g == 0) ws[static_cast<long>(m) * ngroups + tn] = gs.s;
+#pragma unroll
+      for (int h = 0; h < kH; ++h) {
+        const int col = o0 + 32 * wn + 16 * h + 4 * g;
+        const uint32_t code =
+            pack4_e4m3(quotient(v[t][h][0], gs), quotient(v[t][h][1], gs),
+                       quotient(v[t][h][2], gs), quotient(v[t][h][3], gs));
+        *reinterpret_cast<uint32_t*>(q + static_cast<long>(m) * D + col) = code;
+      }
+    }
+    return;
   }
 
   // epilogue: lane holds weight rows n..n+3 of token m
@@ -990,20 +1109,21 @@ std::vector<Variant>& registry() {
 // Raise the dynamic-LDS limit of each kernel once per device (above 64 KiB
 // needs it).  A failure is not remembered, so the next launch retries and
 // the launch itself reports the error.
-void ensure_lds_attr(const Variant& v, int scales) {
-  if (v.lds <= 64 * 1024) return;
+void ensure_fn_lds(const void* fn, size_t lds) {
+  if (lds <= 64 * 1024) return;
   static std::mutex mu;
   static std::vector<std::pair<int, const void*>> done;
-  const void* fn = v.fn[scales];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return;
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& d : done)
     if (d.first == dev && d.second == fn) return;
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(v.lds)) == hipSuccess)
+                          static_cast<int>(lds)) == hipSuccess)
     done.emplace_back(dev, fn);
 }
+
+void ensure_lds_attr(const Variant& v, int scales) { ensure_fn_lds(v.fn[scales], v.lds); }
 
 }  // namespace
 
@@ -1076,6 +1196,21 @@ hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const 
     hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), dim3(blocks), dim3(256), 0, st, y,
                        wsf, sa, sb, M, N, split);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_silu_quant(uint8_t* q, float* scale, const uint8_t* a, const float* sa,
+                                  const uint8_t* b, const float* sb, int M, int N, int K,
+                                  hipStream_t st) {
+  constexpr int kBM = 128, kBN = 256, kWM = 2, kWN = 4, kST = 3;
+  const void* fn = reinterpret_cast<const void*>(
+      &gemm_tiled_kernel<kBM, kBN, kWM, kWN, kST, true, kEngineF16, 0, false, true>);
+  const size_t lds = TiledShape<kBM, kBN, kWM, kWN, kST, true>::kLds;
+  ensure_fn_lds(fn, lds);
+  uint16_t* y = reinterpret_cast<uint16_t*>(q);
+  int split = 1;
+  void* args[] = {&y, &scale, &a, &sa, &b, &sb, &M, &N, &K, &split};
+  const dim3 grid((N / kBN) * ((M + kBM - 1) / kBM), 1);
+  return hipLaunchKernel(fn, grid, dim3(kWM * kWN * 64), args, lds, st);
 }
 
 }  // namespace fp8q

@@ -26,6 +26,7 @@
 // over units (grid-stride) so per-workgroup set-up (the SiLU table in LDS) is
 // amortised.
 #include "fp8q_common.hpp"
+#include "silu_table.hpp"
 #include "quant_kernels.h"
 
 namespace fp8q {
@@ -34,23 +35,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;  // bf16 elements per 16-byte chunk
-
-// Correctly rounded SiLU over bf16 gates: table for |g| in [2^-25, 2^7),
-// closed rules outside it (silu(g) = g/2 exactly in fp32 below 2^-25;
-// silu(g) = g above 2^7; silu(g) rounds to -0 below -2^7).
-__device__ const uint32_t kSiluTable[8192] = {
-#include "silu_table.inc"
-};
-constexpr uint32_t kSiluLo = 102u << 7;  // |g| >= 2^-25
-constexpr uint32_t kSiluHi = 134u << 7;  // |g| <  2^7
-
-__device__ __forceinline__ float silu_bf16(uint32_t bits, const float* tab) {
-  const uint32_t a = bits & 0x7FFFu;
-  const float g = __uint_as_float(bits << 16);
-  if (a < kSiluLo) return g * 0.5f;
-  if (a >= kSiluHi) return (bits & 0x8000u) ? -0.0f : g;
-  return tab[(a - kSiluLo) | ((bits & 0x8000u) >> 3)];
-}
 
 __device__ __forceinline__ void load_silu_table(float* lds) {
   const uint4* src = reinterpret_cast<const uint4*>(kSiluTable);

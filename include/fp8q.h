@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_VERSION 103 /* major*100 + minor */
+#define FP8Q_VERSION 104 /* major*100 + minor */
 
 typedef enum {
   FP8Q_OK = 0,
@@ -209,6 +209,31 @@ int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const float* sa, cons
 /* Bytes of workspace the GEMM `op` needs for this shape with the table's
  * choice (0 when the chosen variant needs none).  Pure host function. */
 size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------
+ * Blockwise GEMM with SiLU-and-mul and group-128 quantization fused into its
+ * epilogue: the MLP's gate_up projection followed by silu_mul_quant (the
+ * blockwise GEMM and the per-block SiLU-and-mul quantizer of the page
+ * "Helion in vLLM: FP8 inference of Qwen3", section "Kernels integrated into
+ * vLLM", one after the other) in one kernel, without writing the bf16
+ * gate_up product to memory.  The results are those of
+ *
+ *   fp8q_scaled_mm_blockwise(y, a, sa, b, sb, M, N, K, ...)   y bf16 [M, N]
+ *   fp8q_silu_mul_quant(q, scale, y, M, N / 2, FP8Q_GROUP128, ...)
+ *
+ * with the GEMM's 128x256-tile variant (the two agree bit for bit).
+ *
+ *   q     [M, N/2]        e4m3 bytes          (out)
+ *   scale [M, N/2/128]    fp32                (out)
+ *   a, sa, b, sb as for fp8q_scaled_mm_blockwise; b holds N rows, the gate
+ *   rows [0, N/2) then the up rows [N/2, N).
+ * Needs N % 256 == 0 and K % 128 == 0; no workspace.  Efficient for large M
+ * (one workgroup per 128 tokens x 128 output columns); correct for every
+ * M >= 0 (M == 0 is a no-op).  Errors as for fp8q_scaled_mm_blockwise.
+ * ---------------------------------------------------------------------- */
+int fp8q_scaled_mm_blockwise_silu_quant(void* q, float* scale, const void* a, const float* sa,
+                                        const void* b, const float* sb, int64_t M, int64_t N,
+                                        int64_t K, void* stream);
 
 /* ------------------------------------------------------------------------
  * GEMM variants.  The same GEMMs with the variant forced instead of taken

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_version() == 103
+    assert L.fp8q_version() == 104
     for s in range(10):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"
@@ -109,6 +109,21 @@ def test_gemm_argument_checks():
     assert need == 4 * 8 * 256 * 4
     assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 4096, None, 0, sp, None) == WS
     assert L.fp8q_scaled_mm_cfg(A, B, C, D, E, 8, 256, 4096, A, need - 1, sp, None) == WS
+
+
+def test_fused_silu_quant_gemm_argument_checks():
+    L = fq.lib()
+    f = L.fp8q_scaled_mm_blockwise_silu_quant
+    # (q, scale, a, sa, b, sb, M, N, K, stream)
+    assert f(A, B, C, D, E, A, 0, 256, 256, None) == OK              # M == 0: no-op
+    assert f(0, 0, 0, 0, 0, 0, 0, 256, 256, None) == OK              # not inspected
+    assert f(A, B, C, D, E, A, -1, 256, 256, None) == INVALID
+    assert f(A, B, C, D, E, A, 4, 0, 256, None) == INVALID
+    assert f(A, B, C, D, E, A, 4, 384, 256, None) == SHAPE           # N/2 not whole groups
+    assert f(A, B, C, D, E, A, 4, 256, 100, None) == SHAPE           # K % 128
+    assert f(A, 0, C, D, E, A, 4, 256, 256, None) == INVALID         # scale
+    assert f(A, B + 4, C, D, E, A, 4, 256, 256, None) == ALIGN
+    assert f(A, B, C, D, 0, A, 4, 256, 256, None) == INVALID         # b
 
 
 def test_int8_argument_checks():
