@@ -19,6 +19,8 @@ namespace {
 thread_local int g_last_hip = 0;
 
 constexpr int kMaxDevices = 64;
+// largest GEMM K: 256 rows of K bytes stay below 2^32
+constexpr int64_t kMaxGemmK = int64_t{1} << 22;
 // per device: 0 unknown, 1 gfx950, 2 other arch; CU count
 std::atomic<int> g_dev_state[kMaxDevices];
 std::atomic<int> g_dev_cus[kMaxDevices];
@@ -94,6 +96,8 @@ int check_gemm_args(int op, const void* y, const void* a, const void* b, const f
     return FP8Q_ERR_ALIGNMENT;
   if (K % 128 != 0 || N % 128 != 0) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return FP8Q_ERR_UNSUPPORTED_SHAPE;
+  // the tiled kernels address a tile's rows with 32-bit byte offsets
+  if (K > kMaxGemmK) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   // int32 sums of int8 products stay exact for K * 127^2 < 2^31
   if (op == FP8Q_OP_SCALED_MM_INT8 && K > 131072) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   return FP8Q_OK;
@@ -221,6 +225,9 @@ int fp8q_scaled_mm_blockwise_silu_quant(void* q, float* scale, const void* a, co
   if (!scale) return FP8Q_ERR_INVALID_ARG;
   if (!aligned16(scale)) return FP8Q_ERR_ALIGNMENT;
   if (N % 256 != 0) return FP8Q_ERR_UNSUPPORTED_SHAPE;  // N/2 whole 128-column groups
+  // a tile's weight rows span its gate rows to its up rows, N/2 rows apart,
+  // addressed with 32-bit byte offsets
+  if ((N / 2 + 128) * K >= (static_cast<int64_t>(1) << 32)) return FP8Q_ERR_UNSUPPORTED_SHAPE;
   int num_cus = 0;
   rc = device_check(&num_cus);
   if (rc != FP8Q_OK) return rc;

@@ -219,6 +219,12 @@ __device__ __forceinline__ void g2lds16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
                : "memory");
 }
+// The same from a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane
+// byte offset: one VGPR per address instead of two.
+__device__ __forceinline__ void g2lds16s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory");
+}
 __device__ __forceinline__ void g2lds4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
                : "memory");
@@ -367,14 +373,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   const int kb_first = static_cast<int>(blockIdx.y) * per_split;
   const int nkb = (KB - kb_first < per_split) ? KB - kb_first : per_split;
 
-  // per-thread, K-block-invariant parts of the load addresses
-  uint32_t a_off[BM * 8 / S::kThreads], b_off[BN * 8 / S::kThreads];
+  // per-thread, K-block-invariant parts of the load addresses: byte offsets
+  // from the workgroup's first token row and first weight row (below
+  // BM * K and BN * K, or (D + 128) * K for SQ; the host checks they fit
+  // in 32 bits)
+  uint32_t a_off[BM * 8 / S::kThreads], b_off0;
 #pragma unroll
   for (int j = 0; j < BM * 8 / S::kThreads; ++j) {
     const int qi = j * S::kThreads + tid;
     const int r = qi >> 3, p = qi & 7;
-    const int row = (m0 + r < M) ? m0 + r : M - 1;
-    a_off[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
+    const int rr = (m0 + r < M) ? r : M - 1 - m0;
+    a_off[j] = static_cast<uint32_t>(rr) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
   }
   static_assert(!SQ || (BLOCK && E == kEngineF16 && !P2 && S::kTN == 64 && WN * 32 == 128),
                 "fused SiLU-and-mul quantization: blockwise exact engine, 128 output columns");
@@ -382,6 +391,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // output column tile, or the matching up row for r % 64 >= 32
   const int D = N / 2;
   const int o0 = tn * 128;  // SQ: first output column of the tile
+  const int nb0 = SQ ? o0 : n0;  // first weight row of the tile's row set
   auto b_row = [&](int r) -> int {
     if constexpr (SQ) {
       const int w = r >> 6, l = r & 63;
@@ -390,11 +400,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       return n0 + r;
     }
   };
-#pragma unroll
-  for (int j = 0; j < BN * 8 / S::kThreads; ++j) {
-    const int qi = j * S::kThreads + tid;
-    const int r = qi >> 3, p = qi & 7;
-    b_off[j] = static_cast<uint32_t>(b_row(r)) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
+  // Weight load j of a thread covers LDS row j * kThreads / 8 + tid / 8,
+  // whose swizzle does not depend on j, and global row b_row of it, which
+  // is kBStep rows further for each j: one offset serves all of them.
+  static_assert((S::kThreads / 8) % 16 == 0, "weight-load rows must keep their swizzle");
+  constexpr int kBStep = SQ ? 32 : S::kThreads / 8;
+  {
+    const int r = tid >> 3, p = tid & 7;
+    b_off0 = static_cast<uint32_t>(b_row(r) - nb0) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
   }
   // blockwise scales: wave w fetches floats [64w, 64w+64) of [sa column | sb | pad]
   const float* s_src = sa;
@@ -414,16 +427,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   }
 
   const uint32_t lds0 = lds_address(smem);
+  const uint8_t* A0 = A + static_cast<long>(m0) * K;
+  const uint8_t* B0 = B + static_cast<long>(nb0) * K;
   auto load_stage = [&](int kb, int buf) {
     const uint32_t base = lds0 + buf * S::kStage + wave * 64 * 16;
-    const uint8_t* Ak = A + static_cast<long>(kb) * kBK;
-    const uint8_t* Bk = B + static_cast<long>(kb) * kBK;
+    const uint8_t* Ak = A0 + static_cast<long>(kb) * kBK;
+    const uint8_t* Bk = B0 + static_cast<long>(kb) * kBK;
 #pragma unroll
     for (int j = 0; j < BM * 8 / S::kThreads; ++j)
-      g2lds16(Ak + a_off[j], base + j * S::kThreads * 16);
+      g2lds16s(Ak, a_off[j], base + j * S::kThreads * 16);
 #pragma unroll
     for (int j = 0; j < BN * 8 / S::kThreads; ++j)
-      g2lds16(Bk + b_off[j], base + S::kXBytes + j * S::kThreads * 16);
+      g2lds16s(Bk + static_cast<long>(j * kBStep) * K, b_off0, base + S::kXBytes + j * S::kThreads * 16);
     if constexpr (BLOCK)
       g2lds4(s_src + s_off + kb, lds0 + buf * S::kStage + S::kXBytes + S::kWBytes + wave * 256);
   };
@@ -484,22 +499,52 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
     for (int t = 0; t < S::kFT; ++t) acc[i][t] = acc_zero<E>();
 
+  // Blockwise scales on the exact engine, without folding: the rotated K
+  // loop below.  Eight-wave tiles run it in two wave groups (see there).
+  constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
+  constexpr bool kGroups = kRotate && S::kWaves == 8 && ST == 3 && !PRIO;
+  // the fused kernel (SQ) needs the registers of half the fragments: it
+  // reads each block's fragments in two halves, the second while the first
+  // is multiplied
+  constexpr bool kHalfReads = kGroups && SQ;
+
+  // the grouped loop issues the same number of loads per block throughout:
+  // past the last block it loads the last block again, into its own buffer
+  // (the same bytes), so its waits are the same constants everywhere
+  auto load_block = [&](int b) {
+    const int bl = (b < nkb) ? b : nkb - 1;
+    load_stage(kb_first + bl, bl % ST);
+  };
 #pragma unroll
-  for (int p = 0; p < ST - 1; ++p)
-    if (p < nkb) load_stage(kb_first + p, p);
+  for (int p = 0; p < ST - 1; ++p) {
+    if constexpr (kGroups)
+      load_block(p);
+    else if (p < nkb)
+      load_stage(kb_first + p, p);
+  }
 
   // the raw fragments and block scales of block j from its LDS buffer (SQ:
   // swr_hi is the up rows' weight scale, swr the gate rows'; else equal)
-  auto read_block = [&](int j, v8i(&xr)[S::kFT], v8i(&wr)[S::kFW], float(&sar)[S::kFT],
-                        float& swr, float& swr_hi) {
+  // half h of the raw fragments of block j: bytes 16h..16h+15 of each
+  // lane's 32, the operands of substeps 2h and 2h+1
+  auto read_half = [&](int j, int h, v4i(&xq)[S::kFT], v4i(&wq)[S::kFW]) {
     const uint8_t* xs = smem + (j % ST) * S::kStage;
     const uint8_t* wsm = xs + S::kXBytes;
 #pragma unroll
-    for (int t = 0; t < S::kFT; ++t) xr[t] = load_frag_lds(xs, wm * S::kTM + 16 * t + lr, g);
+    for (int t = 0; t < S::kFT; ++t) {
+      const int r = wm * S::kTM + 16 * t + lr;
+      xq[t] = *reinterpret_cast<const v4i*>(xs + r * kBK + (((2 * g + h) ^ swz(r)) << 4));
+    }
 #pragma unroll
-    for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(wsm, wn * S::kTN + 16 * i + lr, g);
+    for (int i = 0; i < S::kFW; ++i) {
+      const int r = wn * S::kTN + 16 * i + lr;
+      wq[i] = *reinterpret_cast<const v4i*>(wsm + r * kBK + (((2 * g + h) ^ swz(r)) << 4));
+    }
+  };
+  auto read_scales = [&](int j, float(&sar)[S::kFT], float& swr, float& swr_hi) {
     if constexpr (BLOCK) {
-      const float* sas = reinterpret_cast<const float*>(wsm + S::kWBytes);
+      const float* sas =
+          reinterpret_cast<const float*>(smem + (j % ST) * S::kStage + S::kXBytes + S::kWBytes);
       if constexpr (SQ) {
         swr = sas[BM];
         swr_hi = sas[BM + 1];
@@ -510,6 +555,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) sar[t] = sas[wm * S::kTM + 16 * t + lr];
     }
+  };
+  auto read_block = [&](int j, v8i(&xr)[S::kFT], v8i(&wr)[S::kFW], float(&sar)[S::kFT],
+                        float& swr, float& swr_hi) {
+    const uint8_t* xs = smem + (j % ST) * S::kStage;
+    const uint8_t* wsm = xs + S::kXBytes;
+#pragma unroll
+    for (int t = 0; t < S::kFT; ++t) xr[t] = load_frag_lds(xs, wm * S::kTM + 16 * t + lr, g);
+#pragma unroll
+    for (int i = 0; i < S::kFW; ++i) wr[i] = load_frag_lds(wsm, wn * S::kTN + 16 * i + lr, g);
+    read_scales(j, sar, swr, swr_hi);
   };
 
   // one block's products from its raw fragments and scales
@@ -571,11 +626,92 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // it would exceed 256 VGPRs and halve the occupancy: in the folding
   // kernels, whose folded loop shares the register budget, and in two-wave
   // tiles, whose lanes hold twice the load addresses.)
-  constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
+  // Eight-wave tiles (two waves per SIMD) run the rotated loop with the
+  // waves in two groups half a block apart: waves 4..7 pass one extra
+  // barrier before the loop and waves 0..3 one after it, and every block
+  // has a second barrier after its first two substeps.  Each SIMD holds one
+  // wave of each group, so while one wave waits for its LDS fragments and
+  // applies the previous block's scales (VALU), the other issues matrix
+  // instructions.  In lock step both waves of a SIMD did those at the same
+  // time and the matrix cores idled.  (The mid-block barrier is fenced with
+  // sched_barrier: the compiler would otherwise hoist the second half's
+  // matrix instructions above it.)
+
+  // SQ: once the last block is in flight, the buffer after it is free for
+  // good; the SiLU table (32 KiB: 4 x 1 KiB per wave) goes there while the
+  // last block is multiplied
+  auto prefetch_table = [&](int j) {
+    if constexpr (SQ) {
+      if (j == nkb - 1) {
+        const uint32_t tl = lds0 + ((j + 1) % ST) * S::kStage;
+        const uint8_t* tg = reinterpret_cast<const uint8_t*>(kSiluTable);
+#pragma unroll
+        for (int c = 0; c < 32 / S::kWaves; ++c) {
+          const int chunk = wave * (32 / S::kWaves) + c;
+          g2lds16s(tg + chunk * 1024, lane * 16, tl + chunk * 1024);
+        }
+      }
+    }
+  };
+
+  // The four substeps of one block on the rotated schedule; after_s1()
+  // runs between substeps 1 and 2.  sprev(i, t): the previous block's
+  // scale product for weight fragment i and token fragment t.
+  auto rotated_block = [&](v4f(&p)[S::kFW][S::kFT], auto sprev, const v8i(&xr)[S::kFT],
+                           const v8i(&wr)[S::kFW], auto after_s1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8h xh[S::kFT];
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) xh[t] = widen8(xr[t][2 * s], xr[t][2 * s + 1]);
+#pragma unroll
+      for (int i = 0; i < S::kFW; ++i) {
+        const v8h wh = widen8(wr[i][2 * s], wr[i][2 * s + 1]);
+#pragma unroll
+        for (int t = 0; t < S::kFT; ++t) {
+          if (s == 0) {  // block j-1's products (zeros before the first block)
+            const float sp = sprev(i, t);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
+            p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], v4f{0, 0, 0, 0}, 0, 0, 0);
+          } else {
+            p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], p[i][t], 0, 0, 0);
+          }
+        }
+      }
+      if (s == 1) after_s1();
+    }
+  };
+
+  // substeps 2h and 2h+1 of a block on the rotated schedule, from the
+  // fragment halves (h == 0 applies the previous block's scales first)
+  auto rotated_half = [&](int h, v4f(&p)[S::kFW][S::kFT], auto sprev, const v4i(&xq)[S::kFT],
+                          const v4i(&wq)[S::kFW]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      v8h xh[S::kFT];
+#pragma unroll
+      for (int t = 0; t < S::kFT; ++t) xh[t] = widen8(xq[t][2 * u], xq[t][2 * u + 1]);
+#pragma unroll
+      for (int i = 0; i < S::kFW; ++i) {
+        const v8h wh = widen8(wq[i][2 * u], wq[i][2 * u + 1]);
+#pragma unroll
+        for (int t = 0; t < S::kFT; ++t) {
+          if (h == 0 && u == 0) {
+            const float sp = sprev(i, t);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
+            p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], v4f{0, 0, 0, 0}, 0, 0, 0);
+          } else {
+            p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], p[i][t], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
   auto k_loop_rotated = [&]() {
     v4f p[S::kFW][S::kFT];
-    // block scales of the previous block per token, for the lower and (SQ:
-    // up rows) the upper half of the wave's weight fragments
     float sprev[S::kFT], sprev_hi[S::kFT];
 #pragma unroll
     for (int t = 0; t < S::kFT; ++t) sprev[t] = sprev_hi[t] = 0.0f;
@@ -583,57 +719,110 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     for (int i = 0; i < S::kFW; ++i)
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) p[i][t] = v4f{0, 0, 0, 0};
-    v8i xr[S::kFT], wr[S::kFW];
-    float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
-    for (int j = 0; j < nkb; ++j) {
-      const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
-      wait_stage<S::kLoadsPerStage, ST>(after);
-      __builtin_amdgcn_s_barrier();  // as in the plain loop below
-      asm volatile("" ::: "memory");
-      read_block(j, xr, wr, sar, swr, swr_hi);
-      if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
-      if constexpr (SQ) {
-        // SQ: the buffer after the last block's is free for good; the SiLU
-        // table (32 KiB: 4 x 1 KiB per wave) goes there while the last
-        // block is multiplied
-        if (j == nkb - 1) {
-          const uint32_t tl = lds0 + ((j + 1) % ST) * S::kStage;
-          const uint8_t* tg = reinterpret_cast<const uint8_t*>(kSiluTable);
+    if constexpr (kGroups) {
+      constexpr int L = S::kLoadsPerStage;
+      const bool late = wave >= S::kWaves / 2;
+      // SQ: the previous block's token scales, and its weight scales (the
+      // same for every lane of the wave: kept in scalar registers); their
+      // product is formed where it is applied.  Otherwise sprev/sprev_hi.
+      float sarp[S::kFT], swp = 0.0f, swp_hi = 0.0f;
 #pragma unroll
-          for (int c = 0; c < 32 / S::kWaves; ++c) {
-            const int chunk = wave * (32 / S::kWaves) + c;
-            g2lds16(tg + chunk * 1024 + lane * 16, tl + chunk * 1024);
-          }
-        }
+      for (int t = 0; t < S::kFT; ++t) sarp[t] = 0.0f;
+      auto uniform = [](float v) {
+        return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+      };
+      auto scale_of = [&](int i, int t) {
+        if constexpr (kHalfReads)
+          return sarp[t] * ((SQ && i >= S::kFW / 2) ? swp_hi : swp);
+        else
+          return (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
+      };
+      // before the mid-block barrier this wave's LDS reads of block j have
+      // returned (its buffer is refilled after the next barrier) and its
+      // loads of block j+1 have landed (the other group reads block j+1
+      // after this barrier)
+      auto mid_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vm<L>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // Every block: wait for its loads (one stage of L loads may stay in
+      // flight), barrier, read it, load block j+2 (or the last block again),
+      // substeps 0-1, mid-block barrier, substeps 2-3.  (nkb >= 1: these
+      // tiles are never split along K.)
+      if (late) {
+        wait_vm<L>();
+        __builtin_amdgcn_s_barrier();
       }
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+      for (int j = 0; j < nkb; ++j) {
+        wait_vm<L>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
+        if constexpr (kHalfReads) {
+          v4i xq[S::kFT], wq[S::kFW];
+          read_half(j, 0, xq, wq);
+          read_scales(j, sar, swr, swr_hi);
+          load_block(j + ST - 1);
+          prefetch_table(j);
+          // the reads go out first, ahead of the scale FMAs
+          __builtin_amdgcn_sched_barrier(0);
+          rotated_half(0, p, scale_of, xq, wq);
+          __builtin_amdgcn_sched_barrier(0);
+          read_half(j, 1, xq, wq);
+          mid_barrier();
+          rotated_half(1, p, scale_of, xq, wq);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        v8h xh[S::kFT];
-#pragma unroll
-        for (int t = 0; t < S::kFT; ++t) xh[t] = widen8(xr[t][2 * s], xr[t][2 * s + 1]);
-#pragma unroll
-        for (int i = 0; i < S::kFW; ++i) {
-          const v8h wh = widen8(wr[i][2 * s], wr[i][2 * s + 1]);
+          for (int t = 0; t < S::kFT; ++t) sarp[t] = sar[t];
+          swp = uniform(swr);
+          swp_hi = uniform(swr_hi);
+        } else {
+          v8i xr[S::kFT], wr[S::kFW];
+          read_block(j, xr, wr, sar, swr, swr_hi);
+          load_block(j + ST - 1);
+          prefetch_table(j);
+          rotated_block(p, scale_of, xr, wr, mid_barrier);
 #pragma unroll
           for (int t = 0; t < S::kFT; ++t) {
-            if (s == 0) {  // block j-1's products (zeros before the first block)
-              const float sp = (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
-              p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], v4f{0, 0, 0, 0}, 0, 0, 0);
-            } else {
-              p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], p[i][t], 0, 0, 0);
-            }
+            sprev[t] = sar[t] * swr;
+            sprev_hi[t] = sar[t] * swr_hi;
           }
         }
       }
+      if (!late) __builtin_amdgcn_s_barrier();
+      wait_vm<0>();  // the repeated loads of the last block
+      if constexpr (kHalfReads) {
 #pragma unroll
-      for (int t = 0; t < S::kFT; ++t) {
-        sprev[t] = sar[t] * swr;
-        sprev_hi[t] = sar[t] * swr_hi;
+        for (int t = 0; t < S::kFT; ++t) {
+          sprev[t] = sarp[t] * swp;
+          sprev_hi[t] = sarp[t] * swp_hi;
+        }
       }
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+    } else {
+      v8i xr[S::kFT], wr[S::kFW];
+      float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
+      for (int j = 0; j < nkb; ++j) {
+        const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
+        wait_stage<S::kLoadsPerStage, ST>(after);
+        __builtin_amdgcn_s_barrier();  // as in the plain loop below
+        asm volatile("" ::: "memory");
+        read_block(j, xr, wr, sar, swr, swr_hi);
+        if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
+        prefetch_table(j);
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+        rotated_block(
+            p, [&](int i, int t) { return (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t]; },
+            xr, wr, []() {});
+#pragma unroll
+        for (int t = 0; t < S::kFT; ++t) {
+          sprev[t] = sar[t] * swr;
+          sprev_hi[t] = sar[t] * swr_hi;
+        }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < S::kFW; ++i)

@@ -143,7 +143,7 @@ int fp8q_quant(void* q, float* scale, const void* x, int64_t M, int64_t K, int m
  *   ws / ws_bytes: device workspace of at least
  *                  fp8q_workspace_size(FP8Q_OP_SCALED_MM, M, N, K) bytes;
  *                  may be NULL when that size is 0.
- * Needs K % 128 == 0, N % 128 == 0, K > 0, N > 0.
+ * Needs K % 128 == 0, N % 128 == 0, 0 < K <= 2^22, N > 0.
  * ---------------------------------------------------------------------- */
 int fp8q_scaled_mm(void* y, const void* a, const void* b, const float* sa, const float* sb,
                    int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream);
@@ -158,7 +158,7 @@ int fp8q_scaled_mm(void* y, const void* a, const void* b, const float* sa, const
  *   y  [M, N] bf16 (out)    a [M, K] e4m3 (in)     sa [M, K/128] fp32 (in)
  *   b  [N, K] e4m3 (in)     sb [N/128, K/128] fp32 (in)
  *   ws / ws_bytes as for fp8q_scaled_mm (op FP8Q_OP_SCALED_MM_BLOCKWISE).
- * Needs K % 128 == 0, N % 128 == 0, K > 0, N > 0.
+ * Needs K % 128 == 0, N % 128 == 0, 0 < K <= 2^22, N > 0.
  * ---------------------------------------------------------------------- */
 int fp8q_scaled_mm_blockwise(void* y, const void* a, const float* sa, const void* b,
                              const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
@@ -179,7 +179,7 @@ int fp8q_scaled_mm_blockwise(void* y, const void* a, const float* sa, const void
  *   y[m,n] = bf16( sa[m] * sb[n] * sum_k a[m,k] * b[n,k] ),
  *   a int8 [M, K], b int8 [N, K], sa [M], sb [N] fp32; the integer sum is
  *   exact (int32, so K <= 131072); ws as for fp8q_scaled_mm with
- *   op FP8Q_OP_SCALED_MM_INT8.  Needs K % 128 == 0, N % 128 == 0.
+ *   op FP8Q_OP_SCALED_MM_INT8.  Needs K % 128 == 0, N % 128 == 0, K <= 131072.
  * ---------------------------------------------------------------------- */
 int fp8q_rmsnorm_quant_int8(void* q, float* scale, const void* x, const void* w, int64_t M,
                             int64_t K, float eps, int mode, void* stream);
@@ -227,7 +227,8 @@ size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K);
  *   scale [M, N/2/128]    fp32                (out)
  *   a, sa, b, sb as for fp8q_scaled_mm_blockwise; b holds N rows, the gate
  *   rows [0, N/2) then the up rows [N/2, N).
- * Needs N % 256 == 0 and K % 128 == 0; no workspace.  Efficient for large M
+ * Needs N % 256 == 0, K % 128 == 0 and (N/2 + 128) * K < 2^32; no workspace.
+ * Efficient for large M
  * (one workgroup per 128 tokens x 128 output columns); correct for every
  * M >= 0 (M == 0 is a no-op).  Errors as for fp8q_scaled_mm_blockwise.
  * ---------------------------------------------------------------------- */
