@@ -124,6 +124,18 @@ def test_fused_silu_quant_gemm_argument_checks():
     assert f(A, 0, C, D, E, A, 4, 256, 256, None) == INVALID         # scale
     assert f(A, B + 4, C, D, E, A, 4, 256, 256, None) == ALIGN
     assert f(A, B, C, D, 0, A, 4, 256, 256, None) == INVALID         # b
+    # a tile's rows are addressed with 32-bit byte offsets from its first
+    # gate row: (N/2 + 128) * K must stay below 2^32
+    assert f(A, B, C, D, E, A, 4, 2 * (2**20 - 128), 4096, None) == SHAPE
+    assert f(A, B, C, D, E, A, 4, 2**22, 2**22, None) == SHAPE       # K > 2^22
+
+
+def test_gemm_k_limit():
+    # the tiled kernels address 256 rows of K bytes with 32-bit offsets
+    L = fq.lib()
+    for g in (L.fp8q_scaled_mm_blockwise, L.fp8q_scaled_mm_blockwise_ue8m0):
+        assert g(A, B, C, D, E, 4, 256, 2**22 + 128, None, 0, None) == SHAPE
+    assert L.fp8q_scaled_mm(A, B, C, D, E, 4, 256, 2**22 + 128, None, 0, None) == SHAPE
 
 
 def test_int8_argument_checks():
