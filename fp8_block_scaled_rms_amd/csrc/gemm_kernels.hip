@@ -215,18 +215,14 @@ __device__ __forceinline__ typename AccT<E>::T block_mma(const Frag<E>& w, const
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)p));
 }
-__device__ __forceinline__ void g2lds16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
-               : "memory");
-}
-// The same from a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane
-// byte offset: one VGPR per address instead of two.
+// The global address is a wave-uniform 64-bit base (SGPRs, the `saddr`
+// form) plus a 32-bit per-lane byte offset: one VGPR per address.
 __device__ __forceinline__ void g2lds16s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
                : "memory");
 }
-__device__ __forceinline__ void g2lds4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
+__device__ __forceinline__ void g2lds4s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base)
                : "memory");
 }
 
@@ -358,6 +354,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   using S = TiledShape<BM, BN, WM, WN, ST, BLOCK>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
+  // Blockwise scales on the exact engine, without folding: the rotated K
+  // loop below.  Eight-wave tiles run it in two wave groups (see there).
+  constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
+  constexpr bool kGroups = kRotate && S::kWaves == 8 && ST == 3 && !PRIO;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -377,14 +378,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // from the workgroup's first token row and first weight row (below
   // BM * K and BN * K, or (D + 128) * K for SQ; the host checks they fit
   // in 32 bits)
-  uint32_t a_off[BM * 8 / S::kThreads], b_off0;
+  // Load j of a thread covers LDS row j * kThreads / 8 + tid / 8, whose
+  // swizzle does not depend on j.  Token rows past M are clamped to the
+  // last one.  The eight-wave blockwise tiles, short of registers, derive
+  // every token-row offset from the first (kThreads / 8 rows further per
+  // load, clamped to a_lim; K is a multiple of 128, so the low 7 bits of an
+  // offset are its chunk); the others keep one offset per load.
+  static_assert((S::kThreads / 8) % 16 == 0, "load rows must keep their swizzle");
+  constexpr bool kCompactA = kGroups;
+  constexpr int kALoads = BM * 8 / S::kThreads;
+  uint32_t a_off[kCompactA ? 1 : kALoads], b_off0;
 #pragma unroll
-  for (int j = 0; j < BM * 8 / S::kThreads; ++j) {
+  for (int j = 0; j < (kCompactA ? 1 : kALoads); ++j) {
     const int qi = j * S::kThreads + tid;
     const int r = qi >> 3, p = qi & 7;
     const int rr = (m0 + r < M) ? r : M - 1 - m0;
-    a_off[j] = static_cast<uint32_t>(rr) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
+    a_off[j] = static_cast<uint32_t>(kCompactA ? r : rr) * static_cast<uint32_t>(K) +
+               ((p ^ swz(r)) << 4);
   }
+  const uint32_t a_lim = static_cast<uint32_t>(M - 1 - m0) * static_cast<uint32_t>(K);
   static_assert(!SQ || (BLOCK && E == kEngineF16 && !P2 && S::kTN == 64 && WN * 32 == 128),
                 "fused SiLU-and-mul quantization: blockwise exact engine, 128 output columns");
   // SQ: LDS weight row r (wave r / 64) is gate row 32 (r / 64) + r % 64 of the
@@ -400,30 +412,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       return n0 + r;
     }
   };
-  // Weight load j of a thread covers LDS row j * kThreads / 8 + tid / 8,
-  // whose swizzle does not depend on j, and global row b_row of it, which
-  // is kBStep rows further for each j: one offset serves all of them.
-  static_assert((S::kThreads / 8) % 16 == 0, "weight-load rows must keep their swizzle");
+  // Weight rows: global row b_row of the LDS row, kBStep rows further for
+  // each load (tiles hold whole weight rows: no clamp).
   constexpr int kBStep = SQ ? 32 : S::kThreads / 8;
   {
     const int r = tid >> 3, p = tid & 7;
     b_off0 = static_cast<uint32_t>(b_row(r) - nb0) * static_cast<uint32_t>(K) + ((p ^ swz(r)) << 4);
   }
   // blockwise scales: wave w fetches floats [64w, 64w+64) of [sa column | sb | pad]
-  const float* s_src = sa;
-  long s_off = 0;
+  // (a wave-uniform base: the tile's first token row of sa, or for the wave
+  // holding the sb entries, the tile's first weight block; byte offsets
+  // from it per lane)
+  const int blk0 = SQ ? o0 / 128 : n0 / 128;
+  const float* s_base = (BLOCK && wave == BM / 64) ? sb + static_cast<long>(blk0) * KB
+                                                   : sa + static_cast<long>(m0) * KB;
+  uint32_t s_off = 0;
   if constexpr (BLOCK) {
+    static_assert(BM % 64 == 0 && BN / 128 <= 64, "scale segment layout");
     const int q = wave * 64 + lane;
     if (q < BM) {
-      const int row = (m0 + q < M) ? m0 + q : M - 1;
-      s_off = static_cast<long>(row) * KB;
+      const int rr = (m0 + q < M) ? q : M - 1 - m0;
+      s_off = static_cast<uint32_t>(rr) * static_cast<uint32_t>(KB) * 4u;
     } else if (q < BM + BN / 128) {
-      s_src = sb;
       const int blk = SQ ? (q == BM ? o0 / 128 : (D + o0) / 128) : n0 / 128 + (q - BM);
-      s_off = static_cast<long>(blk) * KB;
-    } else {
-      s_off = static_cast<long>(m0) * KB;  // padding: any valid address
-    }
+      s_off = static_cast<uint32_t>(blk - blk0) * static_cast<uint32_t>(KB) * 4u;
+    }  // else padding: offset 0 from either base is a valid address
   }
 
   const uint32_t lds0 = lds_address(smem);
@@ -434,13 +447,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     const uint8_t* Ak = A0 + static_cast<long>(kb) * kBK;
     const uint8_t* Bk = B0 + static_cast<long>(kb) * kBK;
 #pragma unroll
-    for (int j = 0; j < BM * 8 / S::kThreads; ++j)
-      g2lds16s(Ak, a_off[j], base + j * S::kThreads * 16);
+    for (int j = 0; j < kALoads; ++j) {
+      if constexpr (kCompactA) {
+        const uint32_t o =
+            a_off[0] + static_cast<uint32_t>(j * (S::kThreads / 8)) * static_cast<uint32_t>(K);
+        const uint32_t lim = a_lim + (a_off[0] & 127u);
+        g2lds16s(Ak, o < lim ? o : lim, base + j * S::kThreads * 16);
+      } else {
+        g2lds16s(Ak, a_off[j], base + j * S::kThreads * 16);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < BN * 8 / S::kThreads; ++j)
       g2lds16s(Bk + static_cast<long>(j * kBStep) * K, b_off0, base + S::kXBytes + j * S::kThreads * 16);
     if constexpr (BLOCK)
-      g2lds4(s_src + s_off + kb, lds0 + buf * S::kStage + S::kXBytes + S::kWBytes + wave * 256);
+      g2lds4s(s_base + kb, s_off, lds0 + buf * S::kStage + S::kXBytes + S::kWBytes + wave * 256);
   };
 
   static_assert(!(BLOCK && E == kEngineI8), "the int8 engine is per-token x per-channel only");
@@ -499,14 +520,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
     for (int t = 0; t < S::kFT; ++t) acc[i][t] = acc_zero<E>();
 
-  // Blockwise scales on the exact engine, without folding: the rotated K
-  // loop below.  Eight-wave tiles run it in two wave groups (see there).
-  constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
-  constexpr bool kGroups = kRotate && S::kWaves == 8 && ST == 3 && !PRIO;
-  // the fused kernel (SQ) needs the registers of half the fragments: it
-  // reads each block's fragments in two halves, the second while the first
-  // is multiplied
-  constexpr bool kHalfReads = kGroups && SQ;
+  // the fused kernel (SQ) keeps the previous block's token scales and its
+  // two weight scales (scalar registers) instead of their eight products:
+  // four VGPRs it needs to stay within 256
+  constexpr bool kScalarScales = kGroups && SQ;
 
   // the grouped loop issues the same number of loads per block throughout:
   // past the last block it loads the last block again, into its own buffer
@@ -525,22 +542,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 
   // the raw fragments and block scales of block j from its LDS buffer (SQ:
   // swr_hi is the up rows' weight scale, swr the gate rows'; else equal)
-  // half h of the raw fragments of block j: bytes 16h..16h+15 of each
-  // lane's 32, the operands of substeps 2h and 2h+1
-  auto read_half = [&](int j, int h, v4i(&xq)[S::kFT], v4i(&wq)[S::kFW]) {
-    const uint8_t* xs = smem + (j % ST) * S::kStage;
-    const uint8_t* wsm = xs + S::kXBytes;
-#pragma unroll
-    for (int t = 0; t < S::kFT; ++t) {
-      const int r = wm * S::kTM + 16 * t + lr;
-      xq[t] = *reinterpret_cast<const v4i*>(xs + r * kBK + (((2 * g + h) ^ swz(r)) << 4));
-    }
-#pragma unroll
-    for (int i = 0; i < S::kFW; ++i) {
-      const int r = wn * S::kTN + 16 * i + lr;
-      wq[i] = *reinterpret_cast<const v4i*>(wsm + r * kBK + (((2 * g + h) ^ swz(r)) << 4));
-    }
-  };
   auto read_scales = [&](int j, float(&sar)[S::kFT], float& swr, float& swr_hi) {
     if constexpr (BLOCK) {
       const float* sas =
@@ -683,33 +684,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     }
   };
 
-  // substeps 2h and 2h+1 of a block on the rotated schedule, from the
-  // fragment halves (h == 0 applies the previous block's scales first)
-  auto rotated_half = [&](int h, v4f(&p)[S::kFW][S::kFT], auto sprev, const v4i(&xq)[S::kFT],
-                          const v4i(&wq)[S::kFW]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      v8h xh[S::kFT];
-#pragma unroll
-      for (int t = 0; t < S::kFT; ++t) xh[t] = widen8(xq[t][2 * u], xq[t][2 * u + 1]);
-#pragma unroll
-      for (int i = 0; i < S::kFW; ++i) {
-        const v8h wh = widen8(wq[i][2 * u], wq[i][2 * u + 1]);
-#pragma unroll
-        for (int t = 0; t < S::kFT; ++t) {
-          if (h == 0 && u == 0) {
-            const float sp = sprev(i, t);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
-            p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], v4f{0, 0, 0, 0}, 0, 0, 0);
-          } else {
-            p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], p[i][t], 0, 0, 0);
-          }
-        }
-      }
-    }
-  };
-
   auto k_loop_rotated = [&]() {
     v4f p[S::kFW][S::kFT];
     float sprev[S::kFT], sprev_hi[S::kFT];
@@ -722,9 +696,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     if constexpr (kGroups) {
       constexpr int L = S::kLoadsPerStage;
       const bool late = wave >= S::kWaves / 2;
-      // SQ: the previous block's token scales, and its weight scales (the
-      // same for every lane of the wave: kept in scalar registers); their
-      // product is formed where it is applied.  Otherwise sprev/sprev_hi.
+      // kScalarScales: the previous block's token scales, and its weight
+      // scales (the same for every lane of the wave: kept in scalar
+      // registers); their product is formed where it is applied.  Else
+      // sprev/sprev_hi hold the products.
       float sarp[S::kFT], swp = 0.0f, swp_hi = 0.0f;
 #pragma unroll
       for (int t = 0; t < S::kFT; ++t) sarp[t] = 0.0f;
@@ -732,7 +707,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
       };
       auto scale_of = [&](int i, int t) {
-        if constexpr (kHalfReads)
+        if constexpr (kScalarScales)
           return sarp[t] * ((SQ && i >= S::kFW / 2) ? swp_hi : swp);
         else
           return (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
@@ -762,29 +737,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
-        if constexpr (kHalfReads) {
-          v4i xq[S::kFT], wq[S::kFW];
-          read_half(j, 0, xq, wq);
-          read_scales(j, sar, swr, swr_hi);
-          load_block(j + ST - 1);
-          prefetch_table(j);
-          // the reads go out first, ahead of the scale FMAs
-          __builtin_amdgcn_sched_barrier(0);
-          rotated_half(0, p, scale_of, xq, wq);
-          __builtin_amdgcn_sched_barrier(0);
-          read_half(j, 1, xq, wq);
-          mid_barrier();
-          rotated_half(1, p, scale_of, xq, wq);
+        v8i xr[S::kFT], wr[S::kFW];
+        read_block(j, xr, wr, sar, swr, swr_hi);
+        load_block(j + ST - 1);
+        prefetch_table(j);
+        rotated_block(p, scale_of, xr, wr, mid_barrier);
+        if constexpr (kScalarScales) {
 #pragma unroll
           for (int t = 0; t < S::kFT; ++t) sarp[t] = sar[t];
           swp = uniform(swr);
           swp_hi = uniform(swr_hi);
         } else {
-          v8i xr[S::kFT], wr[S::kFW];
-          read_block(j, xr, wr, sar, swr, swr_hi);
-          load_block(j + ST - 1);
-          prefetch_table(j);
-          rotated_block(p, scale_of, xr, wr, mid_barrier);
 #pragma unroll
           for (int t = 0; t < S::kFT; ++t) {
             sprev[t] = sar[t] * swr;
@@ -794,7 +757,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       }
       if (!late) __builtin_amdgcn_s_barrier();
       wait_vm<0>();  // the repeated loads of the last block
-      if constexpr (kHalfReads) {
+      if constexpr (kScalarScales) {
 #pragma unroll
         for (int t = 0; t < S::kFT; ++t) {
           sprev[t] = sarp[t] * swp;
