@@ -726,8 +726,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       };
       // Every block: wait for its loads (one stage of L loads may stay in
       // flight), barrier, read it, load block j+2 (or the last block again),
-      // substeps 0-1, mid-block barrier, substeps 2-3.  (nkb >= 1: these
-      // tiles are never split along K.)
+      // substeps 0-1, mid-block barrier, substeps 2-3.  (nkb >= 1: a
+      // split along K never leaves a workgroup row without blocks.)
       if (late) {
         wait_vm<L>();
         __builtin_amdgcn_s_barrier();
