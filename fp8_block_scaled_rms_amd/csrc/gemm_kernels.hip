@@ -358,6 +358,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // loop below.  Eight-wave tiles run it in two wave groups (see there).
   constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
   constexpr bool kGroups = kRotate && S::kWaves == 8 && ST == 3 && !PRIO;
+  // the same two-group schedule for the power-of-two folding kernels, whose
+  // block loop is the plain one (weight fragments 0-1, barrier, 2-3)
+  constexpr bool kGroupsP2 = BLOCK && E == kEngineF16 && P2 && S::kWaves == 8 && ST == 3 && !PRIO;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // load, clamped to a_lim; K is a multiple of 128, so the low 7 bits of an
   // offset are its chunk); the others keep one offset per load.
   static_assert((S::kThreads / 8) % 16 == 0, "load rows must keep their swizzle");
-  constexpr bool kCompactA = kGroups;
+  constexpr bool kCompactA = kGroups || kGroupsP2;
   constexpr int kALoads = BM * 8 / S::kThreads;
   uint32_t a_off[kCompactA ? 1 : kALoads], b_off0;
 #pragma unroll
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   };
 #pragma unroll
   for (int p = 0; p < ST - 1; ++p) {
-    if constexpr (kGroups)
+    if constexpr (kGroups || kGroupsP2)
       load_block(p);
     else if (p < nkb)
       load_stage(kb_first + p, p);
@@ -568,9 +571,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     read_scales(j, sar, swr, swr_hi);
   };
 
-  // one block's products from its raw fragments and scales
+  // one block's products from its raw fragments and scales (weight
+  // fragments [I0, I1))
   auto multiply = [&](auto fold_c, const v8i(&xr)[S::kFT], const v8i(&wr)[S::kFW],
-                      const float(&sar)[S::kFT], float swr) {
+                      const float(&sar)[S::kFT], float swr, auto i0, auto i1) {
+    constexpr int I0 = decltype(i0)::value, I1 = decltype(i1)::value;
     constexpr bool FOLD = decltype(fold_c)::value;
     float sab[S::kFT];
     float sxf[S::kFT];
@@ -594,7 +599,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         xf[t] = prep<E>(xr[t]);
     }
 #pragma unroll
-    for (int i = 0; i < S::kFW; ++i) {
+    for (int i = I0; i < I1; ++i) {
       Frag<E> wf;
       if constexpr (FOLD)
         wf = prep_scaled<E>(wr[i], swf);
@@ -800,6 +805,36 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   auto k_loop = [&](auto fold_c) {
     if constexpr (kRotate && !decltype(fold_c)::value) {
       k_loop_rotated();
+    } else if constexpr (kGroupsP2) {
+      // the two-group schedule of k_loop_rotated on the plain block loop
+      constexpr int L = S::kLoadsPerStage;
+      const bool late = wave >= S::kWaves / 2;
+      using H0 = std::integral_constant<int, 0>;
+      using H1 = std::integral_constant<int, S::kFW / 2>;
+      using H2 = std::integral_constant<int, S::kFW>;
+      if (late) {
+        wait_vm<L>();
+        __builtin_amdgcn_s_barrier();
+      }
+      for (int j = 0; j < nkb; ++j) {
+        wait_vm<L>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        v8i xr[S::kFT], wr[S::kFW];
+        float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
+        read_block(j, xr, wr, sar, swr, swr_hi);
+        load_block(j + ST - 1);
+        multiply(fold_c, xr, wr, sar, swr, H0{}, H1{});
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vm<L>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(fold_c, xr, wr, sar, swr, H1{}, H2{});
+      }
+      if (!late) __builtin_amdgcn_s_barrier();
+      wait_vm<0>();  // the repeated loads of the last block
     } else {
       for (int j = 0; j < nkb; ++j) {
         const int after = (nkb - 1 - j < ST - 2) ? nkb - 1 - j : ST - 2;
@@ -816,7 +851,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         // the buffer of block j-1 is free: refill it with block j+ST-1
         if (j + ST - 1 < nkb) load_stage(kb_first + j + ST - 1, (j + ST - 1) % ST);
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
-        multiply(fold_c, xr, wr, sar, swr);
+        multiply(fold_c, xr, wr, sar, swr, std::integral_constant<int, 0>{},
+                 std::integral_constant<int, S::kFW>{});
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
       }
     }
