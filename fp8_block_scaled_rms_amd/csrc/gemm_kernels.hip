@@ -358,9 +358,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // loop below.  Eight-wave tiles run it in two wave groups (see there).
   constexpr bool kRotate = BLOCK && E == kEngineF16 && !P2 && S::kWaves >= 4;
   constexpr bool kGroups = kRotate && S::kWaves == 8 && ST == 3 && !PRIO;
-  // the same two-group schedule for the power-of-two folding kernels, whose
-  // block loop is the plain one (weight fragments 0-1, barrier, 2-3)
-  constexpr bool kGroupsP2 = BLOCK && E == kEngineF16 && P2 && S::kWaves == 8 && ST == 3 && !PRIO;
+  // the same two-group schedule for the eight-wave kernels on the plain
+  // block loop (power-of-two folding, per-token scales, int8): weight
+  // fragments 0-1, barrier, 2-3
+  constexpr bool kGroupsP2 = !kRotate && E != kEngineF8 && S::kWaves == 8 && ST == 3 && !PRIO;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
