@@ -1219,6 +1219,7 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 1>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF16, 1>());
+    v.push_back(tiled_variant<128, 128, 4, 2, 3, kEngineF16>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 4>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 16>());
