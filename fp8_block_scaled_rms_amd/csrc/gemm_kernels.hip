@@ -1270,6 +1270,7 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineI8>());
     v.push_back(tiled_variant<128, 128, 2, 2, 4, kEngineI8>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineI8>());
+    v.push_back(tiled_variant<128, 128, 4, 2, 3, kEngineI8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineI8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineI8, 0, 4>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineI8, 0, 2>());
