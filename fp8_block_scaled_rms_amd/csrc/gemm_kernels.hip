@@ -361,7 +361,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // the same two-group schedule for the eight-wave kernels on the plain
   // block loop (power-of-two folding, per-token scales, int8): weight
   // fragments 0-1, barrier, 2-3
-  constexpr bool kGroupsP2 = !kRotate && E != kEngineF8 && S::kWaves == 8 && ST == 3 && !PRIO;
+  constexpr bool kGroupsPlain = !kRotate && E != kEngineF8 && S::kWaves == 8 && ST == 3 && !PRIO;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   // load, clamped to a_lim; K is a multiple of 128, so the low 7 bits of an
   // offset are its chunk); the others keep one offset per load.
   static_assert((S::kThreads / 8) % 16 == 0, "load rows must keep their swizzle");
-  constexpr bool kCompactA = kGroups || kGroupsP2;
+  constexpr bool kCompactA = kGroups || kGroupsPlain;
   constexpr int kALoads = BM * 8 / S::kThreads;
   uint32_t a_off[kCompactA ? 1 : kALoads], b_off0;
 #pragma unroll
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   };
 #pragma unroll
   for (int p = 0; p < ST - 1; ++p) {
-    if constexpr (kGroups || kGroupsP2)
+    if constexpr (kGroups || kGroupsPlain)
       load_block(p);
     else if (p < nkb)
       load_stage(kb_first + p, p);
@@ -806,7 +806,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
   auto k_loop = [&](auto fold_c) {
     if constexpr (kRotate && !decltype(fold_c)::value) {
       k_loop_rotated();
-    } else if constexpr (kGroupsP2) {
+    } else if constexpr (kGroupsPlain) {
       // the two-group schedule of k_loop_rotated on the plain block loop
       constexpr int L = S::kLoadsPerStage;
       const bool late = wave >= S::kWaves / 2;
