@@ -325,6 +325,27 @@ def test_ue8m0_realistic_against_oracle(M, N, K):
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("name", ["f16_tiled_m128_n256_w2x4_st3", "f16_tiled_m256_n128_w4x2_st3"])
+def test_ue8m0_mixed_folding_waves(name):
+    """Eight-wave tiles whose waves take different paths in one workgroup:
+    token rows with power-of-two scales fold them into the widening, rows
+    with general scales run the per-block FMA, with the same barriers.  Also
+    a ragged M (the last tile's rows clamp) and a long K."""
+    M, N, K = 328, 512, 5120
+    cfg = next(i for i, n in _configs() if n == name)
+    say("ue8m0 mixed folding", name, M, N, K)
+    rng = synth.rng_for("ue8-mixed", name)
+    a = synth.gen_e4m3_codes(rng, (M, K))
+    b = synth.gen_e4m3_codes(rng, (N, K))
+    sa, sb = _scales(rng, BW, M, N, K, pow2=True)
+    sa_gen, _ = _scales(rng, BW, M, N, K)
+    rows = (np.arange(M) // 64) % 2 == 1          # every other 64-row band: general scales
+    sa[rows] = sa_gen[rows]
+    y = bf16_host_f64(_run_ue8(a, sa, b, sb, cfg))
+    res = gemm.acceptance(y, _ref(BW, a, sa, b, sb))
+    assert res["ok"], res
+
+
 def test_ue8m0_falls_back_on_general_or_spread_scales():
     """Scales that are not powers of two take the general path (same bytes as
     scaled_mm_blockwise); so do power-of-two scales whose exponents span more
