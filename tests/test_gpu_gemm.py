@@ -138,6 +138,23 @@ def test_every_tiled_variant_short_k(cfg, name, K):
         _check_engine(name, op, y, a, sa, b, sb)
 
 
+@pytest.mark.parametrize("M", [1, 17, 130])
+@pytest.mark.parametrize("cfg,name", [c for c in _tiled_configs() if c[1].startswith("f16_")],
+                         ids=[n for _, n in _tiled_configs() if n.startswith("f16_")])
+def test_every_tiled_variant_few_tokens(cfg, name, M):
+    """Fewer tokens than a tile (or a ragged last tile): every token-row load
+    past M clamps to the last row, and only rows below M are written."""
+    N, K = 512, 640
+    for op in (MM, BW):
+        say("gemm tiled few tokens", name, op, M, N, K)
+        rng = synth.rng_for("few-tokens", name, op, M, N, K)
+        a = synth.gen_e4m3_codes(rng, (M, K))
+        b = synth.gen_e4m3_codes(rng, (N, K))
+        sa, sb = _scales(rng, op, M, N, K)
+        y = _run(op, a, sa, b, sb, cfg)
+        _check_engine(name, op, y, a, sa, b, sb)
+
+
 @pytest.mark.parametrize("op", [MM, BW], ids=["mm", "blockwise"])
 @pytest.mark.parametrize("cfg,name", _configs(), ids=[n for _, n in _configs()])
 def test_every_variant_one_hot_exact(cfg, name, op):

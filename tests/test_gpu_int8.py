@@ -131,6 +131,22 @@ def test_every_int8_variant(cfg, name):
     _close(y, int8.scaled_mm(a, b, sa, sb))
 
 
+@pytest.mark.parametrize("M", [1, 17, 130])
+@pytest.mark.parametrize("cfg,name", [c for c in _i8_configs() if "_tiled_" in c[1]],
+                         ids=[n for _, n in _i8_configs() if "_tiled_" in n])
+def test_int8_tiled_variant_few_tokens(cfg, name, M):
+    """Fewer tokens than a tile (or a ragged last tile): loads past M clamp
+    to the last row, and only rows below M are written."""
+    N, K = 512, 640
+    say("int8 tiled few tokens", name, M)
+    rng = synth.rng_for("int8-few-tokens", name, M)
+    a, b, sa, sb = _rand_gemm(rng, M, N, K)
+    y = fq.scaled_mm_int8(i8_dev(a), i8_dev(b), f32_dev(sa), f32_dev(sb), cfg=cfg)
+    torch.cuda.synchronize()
+    assert y.shape == (M, N)
+    _close(y, int8.scaled_mm(a, b, sa, sb))
+
+
 @pytest.mark.parametrize("cfg,name", _i8_configs(), ids=[n for _, n in _i8_configs()])
 def test_every_int8_variant_extreme_sums_exact(cfg, name):
     """All operands +-127 (the largest int32 sums) with unit scales and a
