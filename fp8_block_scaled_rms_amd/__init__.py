@@ -34,7 +34,9 @@ OP_SCALED_MM_INT8 = 2
 OP_SCALED_MM_BLOCKWISE_UE8M0 = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+# FP8Q_LIB may name another build of the same library (the host-sanitizer
+# build the CPU tests use); there is no fallback if the file is missing
+LIB_PATH = os.environ.get("FP8Q_LIB") or os.path.join(_HERE, "libfp8q.so")
 
 _STATUS = {
     0: "FP8Q_OK", 1: "FP8Q_ERR_INVALID_ARG", 2: "FP8Q_ERR_UNSUPPORTED_SHAPE",
@@ -47,6 +49,7 @@ _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 _F32 = ctypes.c_float
 _SZ = ctypes.c_size_t
+_PI = ctypes.POINTER(ctypes.c_int)
 
 # name -> (restype, argtypes); the C declarations are in include/fp8q.h
 SIGNATURES = {
@@ -77,7 +80,12 @@ SIGNATURES = {
                                                    _P]),
     "fp8q_cvt_e4m3": (_INT, [_P, _P, _I64, _P]),
     "fp8q_silu": (_INT, [_P, _P, _I64, _P]),
+    "fp8q_quant_launch_config": (_INT, [_INT, _INT, _I64, _I64, _INT, _PI, _PI, _PI]),
     "fp8q_status_string": (ctypes.c_char_p, [_INT]),
+    # ceiling probes (include/fp8q_probe.h)
+    "fp8q_probe_mfma": (_INT, [_INT, _I64, _INT, _P, _P, _P]),
+    "fp8q_probe_mfma_flops_per_iter": (_I64, [_INT]),
+    "fp8q_probe_stream": (_INT, [_INT, _P, _P, _I64, _INT, _P]),
     "fp8q_last_hip_error": (_INT, []),
     "fp8q_version": (_INT, []),
 }
@@ -228,7 +236,7 @@ def fp8q_scaled_mm(y, a, b, sa, sb, ws=None, cfg: int | None = None, stream=None
     _check(rc, "fp8q_scaled_mm")
 
 
-def fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws=None, cfg: int | None = None,
+def fp8q_scaled_mm_blockwise(y, a, b, sa, sb, ws=None, cfg: int | None = None,
                              stream=None) -> None:
     _need(y, _BF16, "y"); _need(a, _E4M3, "a"); _need(b, _E4M3, "b")
     _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
@@ -238,15 +246,15 @@ def fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws=None, cfg: int | None = None,
                 "fp8q_scaled_mm_blockwise")
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     if cfg is None:
-        rc = lib().fp8q_scaled_mm_blockwise(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N,
+        rc = lib().fp8q_scaled_mm_blockwise(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N,
                                             K, _ptr(ws), wsb, _stream(stream))
     else:
-        rc = lib().fp8q_scaled_mm_blockwise_cfg(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M,
+        rc = lib().fp8q_scaled_mm_blockwise_cfg(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M,
                                                 N, K, _ptr(ws), wsb, cfg, _stream(stream))
     _check(rc, "fp8q_scaled_mm_blockwise")
 
 
-def fp8q_scaled_mm_blockwise_ue8m0(y, a, sa, b, sb, ws=None, cfg: int | None = None,
+def fp8q_scaled_mm_blockwise_ue8m0(y, a, b, sa, sb, ws=None, cfg: int | None = None,
                                    stream=None) -> None:
     _need(y, _BF16, "y"); _need(a, _E4M3, "a"); _need(b, _E4M3, "b")
     _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
@@ -256,16 +264,16 @@ def fp8q_scaled_mm_blockwise_ue8m0(y, a, sa, b, sb, ws=None, cfg: int | None = N
                 "fp8q_scaled_mm_blockwise_ue8m0")
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     if cfg is None:
-        rc = lib().fp8q_scaled_mm_blockwise_ue8m0(_ptr(y), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+        rc = lib().fp8q_scaled_mm_blockwise_ue8m0(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
                                                   M, N, K, _ptr(ws), wsb, _stream(stream))
     else:
-        rc = lib().fp8q_scaled_mm_blockwise_ue8m0_cfg(_ptr(y), _ptr(a), _ptr(sa), _ptr(b),
+        rc = lib().fp8q_scaled_mm_blockwise_ue8m0_cfg(_ptr(y), _ptr(a), _ptr(b), _ptr(sa),
                                                       _ptr(sb), M, N, K, _ptr(ws), wsb, cfg,
                                                       _stream(stream))
     _check(rc, "fp8q_scaled_mm_blockwise_ue8m0")
 
 
-def fp8q_scaled_mm_blockwise_silu_quant(q, scale, a, sa, b, sb, stream=None) -> None:
+def fp8q_scaled_mm_blockwise_silu_quant(q, scale, a, b, sa, sb, stream=None) -> None:
     _need(q, _E4M3, "q"); _need(scale, _F32T, "scale"); _need(a, _E4M3, "a")
     _need(b, _E4M3, "b"); _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
     M, K = a.shape
@@ -279,8 +287,8 @@ def fp8q_scaled_mm_blockwise_silu_quant(q, scale, a, sa, b, sb, stream=None) -> 
     _numel(sa, M * (K // 128), f"{what}: sa")
     _numel(sb, (N // 128) * (K // 128), f"{what}: sb")
     _one_device(q, scale, a, sa, b, sb)
-    _check(lib().fp8q_scaled_mm_blockwise_silu_quant(_ptr(q), _ptr(scale), _ptr(a), _ptr(sa),
-                                                     _ptr(b), _ptr(sb), M, N, K,
+    _check(lib().fp8q_scaled_mm_blockwise_silu_quant(_ptr(q), _ptr(scale), _ptr(a), _ptr(b),
+                                                     _ptr(sa), _ptr(sb), M, N, K,
                                                      _stream(stream)), what)
 
 
@@ -363,6 +371,18 @@ def fp8q_version() -> int:
     return lib().fp8q_version()
 
 
+FRONT_IDENT, FRONT_RMSNORM, FRONT_SILU = 0, 1, 2
+
+
+def fp8q_quant_launch_config(front_end: int, mode: int, M: int, K: int, num_cus: int):
+    """(threads per unit, chunks per thread, workgroups) of a quantizer call."""
+    v = [ctypes.c_int(0) for _ in range(3)]
+    _check(lib().fp8q_quant_launch_config(front_end, mode, M, K, num_cus,
+                                          *[ctypes.byref(x) for x in v]),
+           "fp8q_quant_launch_config")
+    return tuple(x.value for x in v)
+
+
 # --------------------------------------------------- allocating helpers --
 
 def _scale_shape(M: int, K: int, mode: int):
@@ -436,22 +456,22 @@ def quant_int8(x, mode: int, stream=None, scale=None):
     return q, s
 
 
-def scaled_mm_blockwise_silu_quant(a, sa, b, sb, stream=None):
+def scaled_mm_blockwise_silu_quant(a, b, sa, sb, stream=None):
     """(q [M, N/2] e4m3, scale [M, N/256] fp32) of silu_mul_quant (group
     128) applied to the blockwise product with the gate rows b[:N/2] and the
     up rows b[N/2:], in one kernel."""
     M, N = a.shape[0], b.shape[0]
     q = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
     s = torch.empty((M, N // 2 // 128), dtype=torch.float32, device=a.device)
-    fp8q_scaled_mm_blockwise_silu_quant(q, s, a, sa, b, sb, stream)
+    fp8q_scaled_mm_blockwise_silu_quant(q, s, a, b, sa, sb, stream)
     return q, s
 
 
-def scaled_mm_blockwise_ue8m0(a, sa, b, sb, cfg: int | None = None, stream=None):
+def scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg: int | None = None, stream=None):
     M, N = a.shape[0], b.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     ws = _workspace(OP_SCALED_MM_BLOCKWISE_UE8M0, M, N, a.shape[1], a.device, cfg)
-    fp8q_scaled_mm_blockwise_ue8m0(y, a, sa, b, sb, ws, cfg, stream)
+    fp8q_scaled_mm_blockwise_ue8m0(y, a, b, sa, sb, ws, cfg, stream)
     return y
 
 
@@ -478,9 +498,9 @@ def scaled_mm(a, b, sa, sb, cfg: int | None = None, stream=None):
     return y
 
 
-def scaled_mm_blockwise(a, sa, b, sb, cfg: int | None = None, stream=None):
+def scaled_mm_blockwise(a, b, sa, sb, cfg: int | None = None, stream=None):
     M, N = a.shape[0], b.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     ws = _workspace(OP_SCALED_MM_BLOCKWISE, M, N, a.shape[1], a.device, cfg)
-    fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws, cfg, stream)
+    fp8q_scaled_mm_blockwise(y, a, b, sa, sb, ws, cfg, stream)
     return y

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -21,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8q.so")
 
-SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "dispatch.cpp", "api.cpp"]
+SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "probe_kernels.hip", "dispatch.cpp",
+           "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -49,11 +51,32 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _run(cmd):
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+def _run(cmd, cwd=None):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                       cwd=cwd)
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}")
     return r.stdout
+
+
+_M0_WORD = re.compile(r"\bm0\b")
+
+
+def check_m0(asm_path: str) -> None:
+    """The GEMM kernels write M0 from inline assembly (the LDS address of a
+    direct global->LDS load) without the compiler knowing.  That is safe only
+    while the compiler itself never keeps a value in M0: every instruction of
+    the generated assembly that names M0 must be one of those writes, each
+    followed by the wait state and the LDS-DMA load that reads it."""
+    with open(asm_path) as f:
+        lines = [ln.split(";")[0].strip() for ln in f]
+    for i, ln in enumerate(lines):
+        if not _M0_WORD.search(ln):
+            continue
+        ok = (re.fullmatch(r"s_mov_b32 m0, s\d+", ln) is not None and i + 2 < len(lines)
+              and lines[i + 1] == "s_nop 0" and lines[i + 2].startswith("global_load_lds_dword"))
+        if not ok:
+            raise RuntimeError(f"{asm_path}:{i + 1}: unexpected use of M0: {ln!r}")
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
@@ -68,16 +91,19 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        # -save-temps keeps the gfx950 assembly next to the object (checked below)
+        cmd = [hipcc, *HIPCC_FLAGS, "-save-temps", "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
-        out = _run(cmd)
+        out = _run(cmd, cwd=BUILD)
         if verbose and out.strip():
             print(out)
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, SOURCES))
+    for src in SOURCES:
+        check_m0(os.path.join(BUILD, os.path.splitext(src)[0] + "-hip-amdgcn-amd-amdhsa-gfx950.s"))
     # 3. link (write to a temp name, then rename: a loaded library is not
     #    clobbered in place)
     tmp = LIB + ".tmp"

@@ -203,22 +203,22 @@ int fp8q_scaled_mm(void* y, const void* a, const void* b, const float* sa, const
   return run_gemm(FP8Q_OP_SCALED_MM, y, a, sa, b, sb, M, N, K, ws, ws_bytes, -1, stream);
 }
 
-int fp8q_scaled_mm_blockwise(void* y, const void* a, const float* sa, const void* b,
+int fp8q_scaled_mm_blockwise(void* y, const void* a, const void* b, const float* sa,
                              const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                              size_t ws_bytes, void* stream) {
   return run_gemm(FP8Q_OP_SCALED_MM_BLOCKWISE, y, a, sa, b, sb, M, N, K, ws, ws_bytes, -1,
                   stream);
 }
 
-int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const float* sa, const void* b,
+int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const void* b, const float* sa,
                                    const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                                    size_t ws_bytes, void* stream) {
   return run_gemm(FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0, y, a, sa, b, sb, M, N, K, ws, ws_bytes,
                   -1, stream);
 }
 
-int fp8q_scaled_mm_blockwise_silu_quant(void* q, float* scale, const void* a, const float* sa,
-                                        const void* b, const float* sb, int64_t M, int64_t N,
+int fp8q_scaled_mm_blockwise_silu_quant(void* q, float* scale, const void* a, const void* b,
+                                        const float* sa, const float* sb, int64_t M, int64_t N,
                                         int64_t K, void* stream) {
   int rc = check_gemm_args(FP8Q_OP_SCALED_MM_BLOCKWISE, q, a, b, sa, sb, M, N, K);
   if (rc != FP8Q_OK || M == 0) return rc;
@@ -237,7 +237,7 @@ int fp8q_scaled_mm_blockwise_silu_quant(void* q, float* scale, const void* a, co
       static_cast<int>(K), static_cast<hipStream_t>(stream)));
 }
 
-int fp8q_scaled_mm_blockwise_ue8m0_cfg(void* y, const void* a, const float* sa, const void* b,
+int fp8q_scaled_mm_blockwise_ue8m0_cfg(void* y, const void* a, const void* b, const float* sa,
                                        const float* sb, int64_t M, int64_t N, int64_t K,
                                        void* ws, size_t ws_bytes, int cfg, void* stream) {
   return run_gemm(FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0, y, a, sa, b, sb, M, N, K, ws, ws_bytes,
@@ -250,7 +250,7 @@ int fp8q_scaled_mm_cfg(void* y, const void* a, const void* b, const float* sa,
   return run_gemm(FP8Q_OP_SCALED_MM, y, a, sa, b, sb, M, N, K, ws, ws_bytes, cfg, stream);
 }
 
-int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const float* sa, const void* b,
+int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const void* b, const float* sa,
                                  const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                                  size_t ws_bytes, int cfg, void* stream) {
   return run_gemm(FP8Q_OP_SCALED_MM_BLOCKWISE, y, a, sa, b, sb, M, N, K, ws, ws_bytes, cfg,
@@ -303,6 +303,24 @@ int fp8q_silu(float* y, const void* g, int64_t n, void* stream) {
   if (rc != FP8Q_OK) return rc;
   return launched(fp8q::launch_silu(y, static_cast<const uint16_t*>(g), static_cast<long>(n),
                                     num_cus, static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_quant_launch_config(int front_end, int mode, int64_t M, int64_t K, int num_cus,
+                             int* tpr, int* ch, int* grid) {
+  if (front_end < fp8q::kIdent || front_end > fp8q::kSilu) return FP8Q_ERR_INVALID_ARG;
+  if (M <= 0 || K <= 0 || num_cus <= 0 || !tpr || !ch || !grid) return FP8Q_ERR_INVALID_ARG;
+  // the same shape checks as the calls (aligned fake pointers: only sizes matter)
+  const int rc = check_quant_args(reinterpret_cast<void*>(16), reinterpret_cast<float*>(16),
+                                  reinterpret_cast<void*>(16), M, K, mode, fp8q::kFmtE4m3);
+  if (rc != FP8Q_OK) return rc;
+  fp8q::QuantLaunch lc;
+  if (!fp8q::quant_launch_config(front_end, mode, static_cast<long>(M), static_cast<int>(K),
+                                 num_cus, &lc))
+    return FP8Q_ERR_UNSUPPORTED_SHAPE;
+  *tpr = lc.tpr;
+  *ch = lc.ch;
+  *grid = lc.grid;
+  return FP8Q_OK;
 }
 
 const char* fp8q_status_string(int status) {

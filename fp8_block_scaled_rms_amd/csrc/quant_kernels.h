@@ -25,6 +25,14 @@ constexpr bool mode_is_ue8(int m) { return m == kPerTokenUe8 || m == kGroup128Ue
 // Largest K (columns of the quantized output) a launch supports.
 int quant_max_k();
 
+// Launch shape of a quantizer call: threads per work unit (64, 128 or 256),
+// 16-byte chunks per thread (the kernel instantiation's CH) and workgroups.
+// Pure host logic; false if no instantiation serves K.
+struct QuantLaunch {
+  int tpr, ch, grid;
+};
+bool quant_launch_config(int op, int mode, long M, int K, int num_cus, QuantLaunch* out);
+
 // q [M,K] e4m3, scale [M] or [M,K/128] (written) or [1] (kStaticTensor:
 // read); x is [M,K] bf16 (kIdent, kRms) or
 // gate_up [M,2K] bf16 (kSilu); w [K] bf16 (kRms only).

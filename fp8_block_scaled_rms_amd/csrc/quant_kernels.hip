@@ -343,9 +343,7 @@ int pick_ch(int chunks_per_thread) {
 
 int quant_max_k() { return kThreads * kChunk * 16; }
 
-hipError_t launch_quant(int op, int mode, int fmt, uint8_t* q, float* scale,
-                        const uint16_t* x, const uint16_t* w, int M, int K, float eps,
-                        int num_cus, hipStream_t st) {
+bool quant_launch_config(int op, int mode, long M, int K, int num_cus, QuantLaunch* out) {
   const bool whole_row = mode_is_row(mode) || (op == kRms);
   const int nchunk = K / kChunk;
   // Chunks a lane may hold before its registers cut occupancy too far (the
@@ -373,12 +371,23 @@ hipError_t launch_quant(int op, int mode, int fmt, uint8_t* q, float* scale,
     ch = pick_ch((nchunk + nseg * 64 - 1) / (nseg * 64));
     unit_chunks = 64 * ch;
   }
-  if (ch < 0) return hipErrorInvalidValue;
+  if (ch < 0) return false;
   const long units = static_cast<long>(M) * ((nchunk + unit_chunks - 1) / unit_chunks);
   const long blocks = (units + (kThreads / tpr) - 1) / (kThreads / tpr);
   // the SiLU table costs 32 KiB of LDS fill per workgroup: fewer, looping ones
   const long cap = static_cast<long>(num_cus) * (op == kSilu ? 4 : 16);
-  const int grid = static_cast<int>(blocks < cap ? blocks : cap);
+  out->tpr = tpr;
+  out->ch = ch;
+  out->grid = static_cast<int>(blocks < cap ? blocks : cap);
+  return true;
+}
+
+hipError_t launch_quant(int op, int mode, int fmt, uint8_t* q, float* scale,
+                        const uint16_t* x, const uint16_t* w, int M, int K, float eps,
+                        int num_cus, hipStream_t st) {
+  QuantLaunch lc;
+  if (!quant_launch_config(op, mode, M, K, num_cus, &lc)) return hipErrorInvalidValue;
+  const int tpr = lc.tpr, ch = lc.ch, grid = lc.grid;
   if (fmt == kFmtI8) {
     if (op == kIdent)
       return launch_quant_mode<kIdent, kFmtI8>(mode, tpr, ch, q, scale, x, w, M, K, eps, grid,

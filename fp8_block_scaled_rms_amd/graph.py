@@ -85,7 +85,7 @@ class LinearChain:
                         M, N, K, ws_p, need)
                 calls.append((L.fp8q_scaled_mm, args, name))
             else:
-                args = (y.data_ptr(), qa.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
+                args = (y.data_ptr(), qa.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(),
                         M, N, K, ws_p, need)
                 calls.append((L.fp8q_scaled_mm_blockwise, args, name))
             if name == "o_proj":
@@ -102,8 +102,8 @@ class LinearChain:
                     self.s_g.data_ptr(), sb.data_ptr(), M, N, K, ws_p, need)
             calls.append((L.fp8q_scaled_mm, args, "down"))
         else:
-            args = (self.y_down.data_ptr(), self.q_g.data_ptr(), self.s_g.data_ptr(),
-                    b.data_ptr(), sb.data_ptr(), M, N, K, ws_p, need)
+            args = (self.y_down.data_ptr(), self.q_g.data_ptr(), b.data_ptr(),
+                    self.s_g.data_ptr(), sb.data_ptr(), M, N, K, ws_p, need)
             calls.append((L.fp8q_scaled_mm_blockwise, args, "down"))
         # execution order: rmsnorm_quant, qkv, quant, o_proj, rmsnorm_quant2, gate_up,
         # silu_mul_quant, down

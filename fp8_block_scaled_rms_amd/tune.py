@@ -119,7 +119,7 @@ def time_shape(op, M, N, K, cands, reps=10):
             elif op == I8:
                 fq.fp8q_scaled_mm_int8(y, a, b, sa, sb, ws, cfg)
             else:
-                fq.fp8q_scaled_mm_blockwise(y, a, sa, b, sb, ws, cfg)
+                fq.fp8q_scaled_mm_blockwise(y, a, b, sa, sb, ws, cfg)
 
         for w in range(2):
             run(bs[w % copies])

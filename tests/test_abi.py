@@ -14,7 +14,7 @@ import torch
 
 import fp8_block_scaled_rms_amd as fq
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fp8q.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 OK, INVALID, SHAPE, ALIGN, WS, NODEV, ARCH, HIP, MODE, CFG = range(10)
 
@@ -22,9 +22,14 @@ A, B, C, D, E = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000  # 16-byte aligned f
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def _no_gpu():
@@ -43,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_version() == 104
+    assert L.fp8q_version() == 200
     for s in range(10):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"
@@ -114,7 +119,7 @@ def test_gemm_argument_checks():
 def test_fused_silu_quant_gemm_argument_checks():
     L = fq.lib()
     f = L.fp8q_scaled_mm_blockwise_silu_quant
-    # (q, scale, a, sa, b, sb, M, N, K, stream)
+    # (q, scale, a, b, sa, sb, M, N, K, stream)
     assert f(A, B, C, D, E, A, 0, 256, 256, None) == OK              # M == 0: no-op
     assert f(0, 0, 0, 0, 0, 0, 0, 256, 256, None) == OK              # not inspected
     assert f(A, B, C, D, E, A, -1, 256, 256, None) == INVALID
@@ -123,7 +128,7 @@ def test_fused_silu_quant_gemm_argument_checks():
     assert f(A, B, C, D, E, A, 4, 256, 100, None) == SHAPE           # K % 128
     assert f(A, 0, C, D, E, A, 4, 256, 256, None) == INVALID         # scale
     assert f(A, B + 4, C, D, E, A, 4, 256, 256, None) == ALIGN
-    assert f(A, B, C, D, 0, A, 4, 256, 256, None) == INVALID         # b
+    assert f(A, B, C, D, 0, A, 4, 256, 256, None) == INVALID         # sa
     # a tile's rows are addressed with 32-bit byte offsets from its first
     # gate row: (N/2 + 128) * K must stay below 2^32
     assert f(A, B, C, D, E, A, 4, 2 * (2**20 - 128), 4096, None) == SHAPE

@@ -44,9 +44,9 @@ def test_gemm_shapes_are_checked():
         fq.fp8q_scaled_mm(_t((8, 64), torch.bfloat16), a, b, _t((8,), torch.float32),
                           _t((128,), torch.float32))
     with pytest.raises(ValueError, match="sa"):
-        fq.fp8q_scaled_mm_blockwise(y, a, _t((8,), torch.float32), b, _t((1, 2), torch.float32))
+        fq.fp8q_scaled_mm_blockwise(y, a, b, _t((8,), torch.float32), _t((1, 2), torch.float32))
     with pytest.raises(ValueError, match="sb"):
-        fq.fp8q_scaled_mm_blockwise(y, a, _t((8, 2), torch.float32), b, _t((3,), torch.float32))
+        fq.fp8q_scaled_mm_blockwise(y, a, b, _t((8, 2), torch.float32), _t((3,), torch.float32))
 
 
 def test_cpu_tensors_are_refused():

@@ -41,7 +41,7 @@ def _case(M, N, K, realistic, seed_tag):
 def _two_kernel(at, sat, bt, sbt):
     M, N = at.shape[0], bt.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    fq.fp8q_scaled_mm_blockwise(y, at, sat, bt, sbt, None, _tile_cfg())
+    fq.fp8q_scaled_mm_blockwise(y, at, bt, sat, sbt, None, _tile_cfg())
     q, s = fq.silu_mul_quant(y, fq.GROUP128)
     return y, q, s
 
@@ -49,7 +49,7 @@ def _two_kernel(at, sat, bt, sbt):
 def _compare(M, N, K, realistic, tag, oracle_rows=None):
     a, sa, b, sb = _case(M, N, K, realistic, tag)
     at, bt, sat, sbt = u8_dev(a), u8_dev(b), f32_dev(sa), f32_dev(sb)
-    qf, sf = fq.scaled_mm_blockwise_silu_quant(at, sat, bt, sbt)
+    qf, sf = fq.scaled_mm_blockwise_silu_quant(at, bt, sat, sbt)
     y, q2, s2 = _two_kernel(at, sat, bt, sbt)
     torch.cuda.synchronize()
     assert torch.equal(qf, q2), int((qf != q2).sum())
@@ -102,13 +102,13 @@ def test_fused_zero_groups_and_m_zero():
     sa = synth.gen_scales(rng, (M, K // 128))
     sb = synth.gen_scales(rng, (N // 128, K // 128))
     at, bt, sat, sbt = u8_dev(a), u8_dev(b), f32_dev(sa), f32_dev(sb)
-    qf, sf = fq.scaled_mm_blockwise_silu_quant(at, sat, bt, sbt)
+    qf, sf = fq.scaled_mm_blockwise_silu_quant(at, bt, sat, sbt)
     _, q2, s2 = _two_kernel(at, sat, bt, sbt)
     torch.cuda.synchronize()
     assert torch.equal(qf, q2) and torch.equal(sf.view(torch.int32), s2.view(torch.int32))
     assert torch.all(sf == 0.0)
     assert torch.all((qf & 0x7F) == 0)
-    q0, s0 = fq.scaled_mm_blockwise_silu_quant(at[:0], sat[:0], bt, sbt)
+    q0, s0 = fq.scaled_mm_blockwise_silu_quant(at[:0], bt, sat[:0], sbt)
     assert q0.shape == (0, N // 2) and s0.shape == (0, N // 256)
 
 
@@ -121,7 +121,7 @@ def test_fused_writes_stay_in_bounds():
     sbuf = torch.full((M * N // 256 + 128,), -7.0, dtype=torch.float32, device=DEV)
     q = qbuf[512:512 + M * N // 2].view(M, N // 2)
     s = sbuf[64:64 + M * N // 256].view(M, N // 256)
-    fq.fp8q_scaled_mm_blockwise_silu_quant(q, s, at, sat, bt, sbt)
+    fq.fp8q_scaled_mm_blockwise_silu_quant(q, s, at, bt, sat, sbt)
     torch.cuda.synchronize()
     assert torch.all(qbuf[:512] == 0x5A) and torch.all(qbuf[512 + M * N // 2:] == 0x5A)
     assert torch.all(sbuf[:64] == -7.0) and torch.all(sbuf[64 + M * N // 256:] == -7.0)

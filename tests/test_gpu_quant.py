@@ -39,7 +39,14 @@ def _check_rms(x, w, mode, rows=None, eps=EPS, scale=None):
     M, K = x.shape
     q, s = fq.rmsnorm_quant(bf16_dev(x), bf16_dev(w), eps, mode, scale=_static(scale))
     torch.cuda.synchronize()
-    q, s = host(q), host(s)
+    return compare_rms(host(q), host(s), x, w, mode, rows, eps, scale)
+
+
+def compare_rms(q, s, x, w, mode, rows=None, eps=EPS, scale=None):
+    """GPU outputs q, s (host arrays, all M rows) of rmsnorm_quant(x, w)
+    against the oracle on `rows` (default all), with the tie policy above.
+    Returns the number of rows accepted under the policy."""
+    M, K = x.shape
     rows = np.arange(M) if rows is None else rows
     qr, sr = quant.rmsnorm_quant(x[rows], w, eps, mode, scale=scale)
     if mode == fq.PER_TENSOR_STATIC:  # the scale is an input: one value, all rows
