@@ -59,6 +59,7 @@ SIGNATURES = {
     "fp8q_scaled_mm": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "fp8q_scaled_mm_blockwise": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "fp8q_workspace_size": (_SZ, [_INT, _I64, _I64, _I64]),
+    "fp8q_scaled_mm_blockwise_noalloc": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8q_gemm_num_configs": (_INT, []),
     "fp8q_gemm_config_name": (ctypes.c_char_p, [_INT]),
     "fp8q_gemm_config_for": (_INT, [_INT, _I64, _I64, _I64]),
@@ -252,6 +253,20 @@ def fp8q_scaled_mm_blockwise(y, a, b, sa, sb, ws=None, cfg: int | None = None,
         rc = lib().fp8q_scaled_mm_blockwise_cfg(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M,
                                                 N, K, _ptr(ws), wsb, cfg, _stream(stream))
     _check(rc, "fp8q_scaled_mm_blockwise")
+
+
+def fp8q_scaled_mm_blockwise_noalloc(y, a, b, sa, sb, stream=None) -> None:
+    """fp8q_scaled_mm_blockwise with the split-K partials in the library's
+    per-GPU scratch array (no workspace argument, nothing allocated)."""
+    _need(y, _BF16, "y"); _need(a, _E4M3, "a"); _need(b, _E4M3, "b")
+    _need(sa, _F32T, "sa"); _need(sb, _F32T, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    _check_gemm(y, a, b, sa, sb, None, M * (K // 128), (N // 128) * (K // 128),
+                "fp8q_scaled_mm_blockwise_noalloc")
+    _check(lib().fp8q_scaled_mm_blockwise_noalloc(_ptr(y), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
+                                                  M, N, K, _stream(stream)),
+           "fp8q_scaled_mm_blockwise_noalloc")
 
 
 def fp8q_scaled_mm_blockwise_ue8m0(y, a, b, sa, sb, ws=None, cfg: int | None = None,

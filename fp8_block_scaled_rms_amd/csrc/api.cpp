@@ -257,6 +257,30 @@ int fp8q_scaled_mm_blockwise_cfg(void* y, const void* a, const void* b, const fl
                   stream);
 }
 
+int fp8q_scaled_mm_blockwise_noalloc(void* y, const void* a, const void* b, const float* sa,
+                                     const float* sb, int64_t M, int64_t N, int64_t K,
+                                     void* stream) {
+  int rc = check_gemm_args(FP8Q_OP_SCALED_MM_BLOCKWISE, y, a, b, sa, sb, M, N, K);
+  if (rc != FP8Q_OK || M == 0) return rc;
+  const int cfg = fp8q::dispatch_gemm(FP8Q_OP_SCALED_MM_BLOCKWISE, M, N, K);
+  if (cfg < 0 || !fp8q::gemm_config_fits(cfg, M, N, K)) return FP8Q_ERR_BAD_CONFIG;
+  const size_t need = fp8q::gemm_workspace_bytes(cfg, M, N, K);
+  if (need > fp8q::kScratchBytes) return FP8Q_ERR_WORKSPACE;
+  int num_cus = 0;
+  rc = device_check(&num_cus);
+  if (rc != FP8Q_OK) return rc;
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = launched(fp8q::scratch_workspace(&ws));
+    if (rc != FP8Q_OK) return rc;
+  }
+  return launched(fp8q::launch_gemm(cfg, fp8q::kScalesBlock, static_cast<uint16_t*>(y),
+                                    static_cast<const uint8_t*>(a), sa,
+                                    static_cast<const uint8_t*>(b), sb, static_cast<int>(M),
+                                    static_cast<int>(N), static_cast<int>(K), ws,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   if (op < FP8Q_OP_SCALED_MM || op > FP8Q_OP_SCALED_MM_BLOCKWISE_UE8M0) return 0;

@@ -55,6 +55,12 @@ hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const 
                        const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
                        hipStream_t st);
 
+// Device address of this GPU's scratch array (kScratchBytes, 256-byte
+// aligned), the split-K workspace of the allocation-free entry point.
+// Looked up once per device (the current one) and cached; no allocation.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+hipError_t scratch_workspace(void** ptr);
+
 // Blockwise GEMM (exact engine, 128x256 tiles) with SiLU-and-mul and
 // group-128 e4m3 quantization in its epilogue: b holds N = 2D weight rows,
 // the gate rows then the up rows; writes q [M, D] e4m3 and scale [M, D/128]

@@ -1111,6 +1111,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict
   }
 }
 
+// ------------------------------------------------------- scratch --
+// Split-K partials of the allocation-free entry point: one array per GPU,
+// resident from the library's load on that device until the process ends.
+// Host code never uses the array's name as an address (on the host it names
+// a stand-in); it takes the device address from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 // ------------------------------------------------------ registry --
 struct Variant {
   GemmConfig cfg;
@@ -1290,6 +1298,26 @@ void ensure_fn_lds(const void* fn, size_t lds) {
 void ensure_lds_attr(const Variant& v, int scales) { ensure_fn_lds(v.fn[scales], v.lds); }
 
 }  // namespace
+
+hipError_t scratch_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *ptr = ptrs[dev];
+  return hipSuccess;
+}
 
 int gemm_num_configs() { return static_cast<int>(registry().size()); }
 const GemmConfig& gemm_config(int id) { return registry()[id].cfg; }

@@ -207,6 +207,30 @@ int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const void* b, const 
                                    const float* sb, int64_t M, int64_t N, int64_t K, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * fp8q_scaled_mm_blockwise for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc.  Same operands, result and errors as fp8q_scaled_mm_blockwise
+ * (the same kernels; results identical bit for bit), without ws/ws_bytes:
+ * when the table's variant for the shape splits K across workgroups, its
+ * fp32 partials go to a scratch array the library holds on each GPU it runs
+ * on (FP8Q_NOALLOC_SCRATCH_BYTES, resident until the process ends) instead
+ * of a caller workspace.  The call allocates nothing and records no memset
+ * (every partial is written before it is read).
+ * Returns FP8Q_ERR_WORKSPACE, before touching the device, when the shape's
+ * variant needs more than FP8Q_NOALLOC_SCRATCH_BYTES of partials, i.e. when
+ * fp8q_workspace_size(FP8Q_OP_SCALED_MM_BLOCKWISE, M, N, K) exceeds it (the
+ * decode and small-M shapes need at most 20 MiB; long-K shapes at large M
+ * can need more).
+ * All calls on one GPU share its scratch array: calls whose executions
+ * overlap on one GPU (concurrent streams, or threads) race on it and give
+ * undefined results.  Calls ordered on one stream are safe.
+ * ---------------------------------------------------------------------- */
+#define FP8Q_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fp8q_scaled_mm_blockwise_noalloc(void* y, const void* a, const void* b, const float* sa,
+                                     const float* sb, int64_t M, int64_t N, int64_t K,
+                                     void* stream);
+
 /* Bytes of workspace the GEMM `op` needs for this shape with the table's
  * choice (0 when the chosen variant needs none).  Pure host function. */
 size_t fp8q_workspace_size(int op, int64_t M, int64_t N, int64_t K);

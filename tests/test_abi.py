@@ -135,6 +135,23 @@ def test_fused_silu_quant_gemm_argument_checks():
     assert f(A, B, C, D, E, A, 4, 2**22, 2**22, None) == SHAPE       # K > 2^22
 
 
+def test_noalloc_gemm_argument_checks():
+    L = fq.lib()
+    f = L.fp8q_scaled_mm_blockwise_noalloc
+    assert f(A, B, C, D, E, 0, 256, 256, None) == OK
+    assert f(A, B, C, D, E, -1, 256, 256, None) == INVALID
+    assert f(A, B, C, D, E, 4, 200, 256, None) == SHAPE
+    assert f(A + 2, B, C, D, E, 4, 256, 256, None) == ALIGN
+    # a shape whose table variant needs more split-K partials than the
+    # scratch array holds is refused on the host, before any device call
+    M, N, K = 2048, 5120, 25600
+    assert fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, M, N, K) > 64 << 20
+    assert f(A, B, C, D, E, M, N, K, None) == WS
+    # every decode / small-M shape of the workloads fits
+    for M, N, K in ((32, 24576, 4096), (64, 5120, 25600), (32, 4096, 12288)):
+        assert 0 < fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, M, N, K) <= 64 << 20
+
+
 def test_gemm_k_limit():
     # the tiled kernels address 256 rows of K bytes with 32-bit offsets
     L = fq.lib()
@@ -182,6 +199,7 @@ def test_valid_calls_report_no_device_without_gpu():
     assert L.fp8q_quant(A, B, C, 4, 128, 1, None) == NODEV
     assert L.fp8q_scaled_mm(A, B, C, D, E, 4, 256, 256, None, 0, None) == NODEV
     assert L.fp8q_scaled_mm_blockwise(A, B, C, D, E, 4, 256, 256, None, 0, None) == NODEV
+    assert L.fp8q_scaled_mm_blockwise_noalloc(A, B, C, D, E, 4, 256, 256, None) == NODEV
     assert L.fp8q_cvt_e4m3(A, B, 16, None) == NODEV
     assert L.fp8q_silu(A, B, 16, None) == NODEV
     assert L.fp8q_quant_int8(A, B, C, 4, 128, 0, None) == NODEV

@@ -1,0 +1,69 @@
+"""The allocation-free blockwise GEMM (fp8q_scaled_mm_blockwise_noalloc,
+called through the C ABI) against fp8q_scaled_mm_blockwise with a caller
+workspace: the same kernels, so the outputs must be identical bit for bit.
+Two calls in a row on split-K shapes, the second smaller than the first
+(the scratch array then still holds the first call's partials), and a shape
+whose variant needs no workspace."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_rms_amd as fq
+import synth
+from gpu_util import DEV, say
+
+pytestmark = pytest.mark.gpu
+
+BW = fq.OP_SCALED_MM_BLOCKWISE
+
+
+def _operands(M, N, K, tag):
+    rng = synth.rng_for("noalloc", tag, M, N, K)
+    a = torch.from_numpy(synth.gen_e4m3_codes(rng, (M, K))).to(DEV)
+    b = torch.from_numpy(synth.gen_e4m3_codes(rng, (N, K))).to(DEV)
+    sa = torch.from_numpy(synth.gen_scales(rng, (M, K // 128))).to(DEV)
+    sb = torch.from_numpy(synth.gen_scales(rng, (N // 128, K // 128))).to(DEV)
+    return a, b, sa, sb
+
+
+def _both(M, N, K, tag):
+    L = fq.lib()
+    a, b, sa, sb = _operands(M, N, K, tag)
+    st = torch.cuda.current_stream().cuda_stream
+    need = fq.fp8q_workspace_size(BW, M, N, K)
+    ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device=DEV)
+    y_ref = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    rc = L.fp8q_scaled_mm_blockwise(y_ref.data_ptr(), a.data_ptr(), b.data_ptr(), sa.data_ptr(),
+                                    sb.data_ptr(), M, N, K, ws.data_ptr(), need, st)
+    assert rc == 0, rc
+    y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    rc = L.fp8q_scaled_mm_blockwise_noalloc(y.data_ptr(), a.data_ptr(), b.data_ptr(),
+                                            sa.data_ptr(), sb.data_ptr(), M, N, K, st)
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    return y, y_ref, need
+
+
+@pytest.mark.parametrize("first,second", [((64, 5120, 25600), (32, 4096, 12288)),
+                                          ((32, 24576, 4096), (8, 4096, 12288))])
+def test_noalloc_matches_workspace_path_twice(first, second):
+    for i, (M, N, K) in enumerate((first, second)):
+        say("noalloc", i, M, N, K)
+        y, y_ref, need = _both(M, N, K, f"call{i}")
+        assert need > 0  # these shapes split K: the scratch array is used
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (M, N, K)
+
+
+def test_noalloc_without_split_k():
+    M, N, K = 200, 1024, 1024
+    y, y_ref, need = _both(M, N, K, "nosplit")
+    assert need == 0
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+
+
+def test_noalloc_rejects_oversized_partials():
+    M, N, K = 2048, 5120, 25600
+    a = torch.empty((1,), dtype=torch.uint8, device=DEV)
+    rc = fq.lib().fp8q_scaled_mm_blockwise_noalloc(a.data_ptr(), a.data_ptr(), a.data_ptr(),
+                                                   a.data_ptr(), a.data_ptr(), M, N, K, None)
+    assert rc == 4  # FP8Q_ERR_WORKSPACE, nothing launched
