@@ -22,7 +22,8 @@ OUT = os.path.join(b.BUILD, "asan")
 HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
                  "-fno-omit-frame-pointer"]
-KERNEL_OBJECTS = ["quant_kernels.o", "gemm_kernels.o", "probe_kernels.o"]
+# the ordinary build's objects of every HIP source (kernels and their launchers)
+KERNEL_OBJECTS = [src.replace(".hip", ".o") for src in b.SOURCES if src.endswith(".hip")]
 
 
 def _asan_runtime(hipcc):
