@@ -32,6 +32,8 @@ and replayed from a HIP graph, w8a8_int8 the int8 GEMMs on the Qwen3-1.7B
 shapes, and ue8m0_blockwise the prefill GEMMs with power-of-two scales.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --decode-study   small-M GEMMs beside a read-only kernel
+                                        streaming the same weight bytes
 """
 from __future__ import annotations
 
@@ -132,6 +134,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--detail", default=None, help="write a per-kernel breakdown JSON here")
     p.add_argument("--cpu-sample-rows", type=int, default=2048)
+    p.add_argument("--decode-study", action="store_true",
+                   help="only time the small-M (HBM-bound) GEMM launches of a step, each beside "
+                        "a read-only kernel streaming the same weight bytes, and print that "
+                        "comparison as one JSON line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (3 times), the known-size "
                         "reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -487,6 +493,61 @@ def per_kernel_times(step: Step, batches: int = 3):
     return out
 
 
+def decode_study(step: Step, reps: int = 50):
+    """Every small-M GEMM launch of a step (the 8B block decode, the 32B MLP
+    tail at M=64, the 1.7B gate_up at M<=128) timed as in per_kernel_times,
+    beside the read-only probe kernel (include/fp8q_probe.h) streaming the
+    same weight bytes from the same rotated copies: the gap is what the GEMM
+    costs beyond reading its weights."""
+    torch, L = step.torch, step.lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * cus * 256, dtype=torch.int32, device=step.dev)
+    out = {}
+    for label, kind, flops, nbytes, call in step.calls:
+        wl, M = label.split("/")[0], int(label.split("/")[1][1:])
+        small = flops and (wl == "qwen3-8b-block-decode" or
+                           (wl == "qwen3-32b-mlp-tail" and M == 64) or
+                           (wl == "qwen3-1.7b-per-token" and label.endswith("/gate_up")
+                            and M <= 128))
+        if not small:
+            continue
+        (pos, wt), = call.rot.items()
+        wbytes = wt.numel() * wt.element_size()
+        copies = int(min(reps, max(1, -(-ROTATE_BYTES // wbytes))))
+        pool = torch.empty((copies,) + tuple(wt.shape), dtype=wt.dtype, device=step.dev)
+        pool.copy_(wt.unsqueeze(0).expand_as(pool))
+        ptrs = [pool[i].data_ptr() for i in range(copies)]
+        res = {"bytes": int(nbytes), "weight_bytes": int(wbytes)}
+        for what in ("gemm", "read_only"):
+            def run(r):
+                if what == "gemm":
+                    call({pos: ptrs[r % copies]})
+                else:
+                    rc = L.fp8q_probe_stream(2, ptrs[r % copies], sink.data_ptr(), wbytes,
+                                             8 * cus, step.stream)
+                    if rc != 0:
+                        raise RuntimeError(f"probe_stream status {rc}")
+            run(0)
+            ts = []
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                queue_ahead(torch, 2_000_000 + 60_000 * reps)
+                e0.record()
+                for r in range(reps):
+                    run(r)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+            res[f"{what}_us"] = round(float(np.median(ts)), 2)
+        res["gemm_gbs"] = round(nbytes / res["gemm_us"] / 1e3, 0)
+        res["read_only_gbs"] = round(wbytes / res["read_only_us"] / 1e3, 0)
+        res["gemm_over_read_only"] = round(res["gemm_us"] / res["read_only_us"], 3)
+        out[label] = res
+        del pool
+    return out
+
+
 def measure_ceilings(step: Step):
     """What this GPU reaches on plain loops (include/fp8q_probe.h): dense
     f16 and FP8 matrix instructions on every CU (and the shader clock
@@ -747,6 +808,15 @@ def main():
     step = Step(fq, torch, dev)
     cfg_of = build(step)
     total_flops = sum(c[2] for c in step.calls)
+    if args.decode_study:
+        for _ in range(2):
+            step.run()
+        torch.cuda.synchronize()
+        study = decode_study(step)
+        for label in study:
+            study[label]["variant"] = variant_name(fq, cfg_of.get(label))
+        print(json.dumps({"decode_study": study}), flush=True)
+        return
 
     # warm up, then find the dominant kernel from one event-timed pass
     for _ in range(args.warmup):

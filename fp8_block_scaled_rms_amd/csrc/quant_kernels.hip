@@ -89,8 +89,15 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
   return pack4_e4m3(a, b, c, d);
 }
 
+// Waves per SIMD the register allocation must leave room for: streaming
+// needs many waves in flight, which the scheduler otherwise trades for
+// instruction-level parallelism across chunks (6 waves: <= 85 VGPRs).
+template <int CH>
+constexpr int quant_waves() { return CH <= 6 ? 6 : 2; }
+
 template <int OP, int MODE, int TPR, int CH, int FMT>
-__global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads)
+void quant_kernel(uint8_t* __restrict__ q,
                                                          float* __restrict__ scale,
                                                          const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w, int M,
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
     const int c_end = (c0 + unit_chunks < nchunk) ? c0 + unit_chunks : nchunk;
     const uint16_t* xr = x + row * in_stride;
 
-    // ---- load (all chunks first) and front end: y (fp32) per element
+    // ---- load (all chunks first): x (or the gate), and w (or the up half)
     uint4 xv[CH], wv[CH];
     bool valid[CH];
 #pragma unroll
@@ -136,56 +143,97 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
       if constexpr (OP == kSilu)
         wv[i] = valid[i] ? *reinterpret_cast<const uint4*>(xr + K + c * kChunk)
                          : make_uint4(0, 0, 0, 0);  // up
+      if constexpr (OP == kIdent) wv[i] = make_uint4(0, 0, 0, 0);  // unused
     }
-    float y[CH][kChunk];
-    double ss = 0.0;
+    // ---- RMSNorm: fp64 sum of squares over the row, then the inverse RMS
+    float inv = 1.0f;
+    if constexpr (OP == kRms) {
+      double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
+      for (int i = 0; i < CH; ++i) {
+        const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const double d0 = bf16_lo(vv[j]), d1 = bf16_hi(vv[j]);
+          ss = fma(d0, d0, ss);
+          ss = fma(d1, d1, ss);
+        }
+      }
+      const double tot = unit_sum<TPR>(ss, red64);
+      const double t = tot / static_cast<double>(K) + static_cast<double>(eps);
+      inv = static_cast<float>(1.0 / sqrt(t));
+    }
+
+    // ---- y (fp32) of chunk i.  SiLU-and-mul in a per-token mode needs every
+    // y twice (for the row's amax, then for the quotients) and keeps them;
+    // every other case forms a chunk's y where it is used, from the raw bf16
+    // registers, with the same operations in the same order (for RMSNorm
+    // RN32(RN32(x * w) * inv), x * w exact), keeping 8 fewer registers live
+    // per chunk.
+    constexpr bool kKeepY = (OP == kSilu) && !mode_is_group(MODE);
+    auto form_y = [&](int i, float(&yo)[kChunk]) {
       const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
       const uint32_t ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (OP == kIdent) {
-          y[i][2 * j] = bf16_lo(vv[j]);
-          y[i][2 * j + 1] = bf16_hi(vv[j]);
+          yo[2 * j] = bf16_lo(vv[j]);
+          yo[2 * j + 1] = bf16_hi(vv[j]);
         } else if constexpr (OP == kRms) {
-          const float x0 = bf16_lo(vv[j]), x1 = bf16_hi(vv[j]);
-          const double d0 = x0, d1 = x1;
-          ss = fma(d0, d0, ss);
-          ss = fma(d1, d1, ss);
-          y[i][2 * j] = x0 * bf16_lo(ww[j]);  // exact in fp32
-          y[i][2 * j + 1] = x1 * bf16_hi(ww[j]);
+          yo[2 * j] = (bf16_lo(vv[j]) * bf16_lo(ww[j])) * inv;  // x * w exact in fp32
+          yo[2 * j + 1] = (bf16_hi(vv[j]) * bf16_hi(ww[j])) * inv;
         } else {  // kSilu: gate in xv, up in wv
-          y[i][2 * j] = silu_bf16(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(ww[j]);
-          y[i][2 * j + 1] = silu_bf16(vv[j] >> 16, silu_tab) * bf16_hi(ww[j]);
+          yo[2 * j] = silu_bf16(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(ww[j]);
+          yo[2 * j + 1] = silu_bf16(vv[j] >> 16, silu_tab) * bf16_hi(ww[j]);
         }
       }
+    };
+    float ykeep[kKeepY ? CH : 1][kChunk];
+    if constexpr (kKeepY) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) form_y(i, ykeep[i]);
     }
-
-    if constexpr (OP == kRms) {
-      const double tot = unit_sum<TPR>(ss, red64);
-      const double t = tot / static_cast<double>(K) + static_cast<double>(eps);
-      const float inv = static_cast<float>(1.0 / sqrt(t));
+    auto chunk_y = [&](int i, float(&yo)[kChunk]) {
+      if constexpr (kKeepY) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i)
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) y[i][j] = y[i][j] * inv;
-    }
-
-    // ---- amax per chunk, then per group (16 lanes) or per row
-    float cmax[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
+        for (int j = 0; j < kChunk; ++j) yo[j] = ykeep[i][j];
+      } else {
+        form_y(i, yo);
+      }
+    };
+    auto chunk_amax = [&](const float(&yo)[kChunk]) {
       float m = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) m = fmaxf(m, fabsf(y[i][j]));
-      cmax[i] = valid[i] ? m : 0.0f;
-    }
+      for (int j = 0; j < kChunk; ++j) m = fmaxf(m, fabsf(yo[j]));
+      return m;
+    };
+    auto store_chunk = [&](int i, const float(&yo)[kChunk], const GroupScale& g) {
+      const int c = c0 + tid + i * TPR;
+      uint2 out;
+      if constexpr (MODE == kStaticTensor) {
+        out.x = pack4<FMT>(quotient_static(yo[0], g), quotient_static(yo[1], g),
+                           quotient_static(yo[2], g), quotient_static(yo[3], g));
+        out.y = pack4<FMT>(quotient_static(yo[4], g), quotient_static(yo[5], g),
+                           quotient_static(yo[6], g), quotient_static(yo[7], g));
+      } else {
+        out.x = pack4<FMT>(quotient(yo[0], g), quotient(yo[1], g), quotient(yo[2], g),
+                           quotient(yo[3], g));
+        out.y = pack4<FMT>(quotient(yo[4], g), quotient(yo[5], g), quotient(yo[6], g),
+                           quotient(yo[7], g));
+      }
+      *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
+    };
 
     if constexpr (mode_is_row(MODE)) {
-      float m = cmax[0];
+      // amax over the row, then the quotients
+      float m = 0.0f;
 #pragma unroll
-      for (int i = 1; i < CH; ++i) m = fmaxf(m, cmax[i]);
+      for (int i = 0; i < CH; ++i) {
+        if (!valid[i]) continue;
+        float yo[kChunk];
+        chunk_y(i, yo);
+        m = fmaxf(m, chunk_amax(yo));
+      }
       const float amax = unit_max<TPR>(m, red32);
       const GroupScale g = FMT == kFmtI8      ? make_scale_i8(amax)
                            : mode_is_ue8(MODE) ? make_scale_ue8m0(amax)
@@ -194,42 +242,32 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(uint8_t* __restrict__ q
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         if (!valid[i]) continue;
-        const int c = c0 + tid + i * TPR;
-        uint2 out;
-        out.x = pack4<FMT>(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
-                           quotient(y[i][3], g));
-        out.y = pack4<FMT>(quotient(y[i][4], g), quotient(y[i][5], g), quotient(y[i][6], g),
-                           quotient(y[i][7], g));
-        *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
+        float yo[kChunk];
+        chunk_y(i, yo);
+        store_chunk(i, yo, g);
       }
     } else if constexpr (mode_is_group(MODE)) {
+      // one 128-group per chunk and 16 lanes: its amax, scale and codes
       const int ngroups = K / kGroup;
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
-        const float amax = max16(cmax[i]);  // all 16 lanes of a group agree
+        float yo[kChunk];
+        chunk_y(i, yo);
+        const float amax = max16(valid[i] ? chunk_amax(yo) : 0.0f);  // all 16 lanes agree
         if (!valid[i]) continue;
         const int c = c0 + tid + i * TPR;
         const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
         if ((tid & 15) == 0) scale[static_cast<long>(row) * ngroups + c / 16] = g.s;
-        uint2 out;
-        out.x = pack4<FMT>(quotient(y[i][0], g), quotient(y[i][1], g), quotient(y[i][2], g),
-                           quotient(y[i][3], g));
-        out.y = pack4<FMT>(quotient(y[i][4], g), quotient(y[i][5], g), quotient(y[i][6], g),
-                           quotient(y[i][7], g));
-        *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
+        store_chunk(i, yo, g);
       }
     } else {  // kStaticTensor: the caller's scale, read once per unit
       const GroupScale g = static_scale(scale[0]);
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         if (!valid[i]) continue;
-        const int c = c0 + tid + i * TPR;
-        uint2 out;
-        out.x = pack4<FMT>(quotient_static(y[i][0], g), quotient_static(y[i][1], g),
-                           quotient_static(y[i][2], g), quotient_static(y[i][3], g));
-        out.y = pack4<FMT>(quotient_static(y[i][4], g), quotient_static(y[i][5], g),
-                           quotient_static(y[i][6], g), quotient_static(y[i][7], g));
-        *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
+        float yo[kChunk];
+        chunk_y(i, yo);
+        store_chunk(i, yo, g);
       }
     }
   }
@@ -279,6 +317,7 @@ hipError_t launch_quant_ch(int ch, uint8_t* q, float* scale, const uint16_t* x,
     case 1: return launch_quant_t<OP, MODE, TPR, 1, FMT>(q, scale, x, w, M, K, eps, grid, st);
     case 2: return launch_quant_t<OP, MODE, TPR, 2, FMT>(q, scale, x, w, M, K, eps, grid, st);
     case 4: return launch_quant_t<OP, MODE, TPR, 4, FMT>(q, scale, x, w, M, K, eps, grid, st);
+    case 5: return launch_quant_t<OP, MODE, TPR, 5, FMT>(q, scale, x, w, M, K, eps, grid, st);
     case 6: return launch_quant_t<OP, MODE, TPR, 6, FMT>(q, scale, x, w, M, K, eps, grid, st);
     case 8: return launch_quant_t<OP, MODE, TPR, 8, FMT>(q, scale, x, w, M, K, eps, grid, st);
     case 10: return launch_quant_t<OP, MODE, TPR, 10, FMT>(q, scale, x, w, M, K, eps, grid, st);
@@ -333,7 +372,7 @@ hipError_t launch_quant_mode(int mode, int tpr, int ch, uint8_t* q, float* scale
 }
 
 int pick_ch(int chunks_per_thread) {
-  static const int kAllowed[] = {1, 2, 4, 6, 8, 10, 12, 16};
+  static const int kAllowed[] = {1, 2, 4, 5, 6, 8, 10, 12, 16};
   for (int c : kAllowed)
     if (c >= chunks_per_thread) return c;
   return -1;
