@@ -237,14 +237,6 @@ __device__ __forceinline__ v8i load_frag_lds(const uint8_t* tile, int r, int g) 
   return f;
 }
 
-__device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  v8i f;
-  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
-  return f;
-}
 
 
 
@@ -958,24 +950,33 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
   const int KB = K / kBK;
   const int kb0 = s * (WK * J) + wave;  // this wave: kb0, kb0 + WK, ...
 
-  const uint8_t* wrow[RW];
-#pragma unroll
-  for (int i = 0; i < RW; ++i) wrow[i] = B + static_cast<long>(n0 + 16 * i + lr) * K + 32 * g;
-  const uint8_t* xrow[TMX];
+  // Fragments are loaded through buffer resources over this workgroup's
+  // weight rows and over the M token rows (offsets below 2^32: K <= 2^22,
+  // at most 64 weight rows and 128 tokens).  A token row at or beyond M, or
+  // a block past K (offset kOutside), lies outside its resource and loads
+  // zeros without touching memory.
+  const __amdgpu_buffer_rsrc_t wres =
+      buffer_rsrc(B + static_cast<long>(n0) * K, static_cast<uint32_t>(RW * 16) * K);
+  const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(A, static_cast<uint32_t>(M) * K);
+  constexpr uint32_t kOutside = 0x80000000u;
+  uint32_t woff[RW], xoff[TMX];
   bool xok[TMX];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) woff[i] = static_cast<uint32_t>(16 * i + lr) * K + 32 * g;
 #pragma unroll
   for (int t = 0; t < TMX; ++t) {
     const int m = 16 * t + lr;
     xok[t] = m < M;
-    xrow[t] = A + static_cast<long>(xok[t] ? m : 0) * K + 32 * g;
+    xoff[t] = static_cast<uint32_t>(m) * K + 32 * g;
   }
   const long sb_row = static_cast<long>(n0 / 128) * KB;
 
-  // issue every load of this wave first.  The block scales are loaded
-  // unconditionally from clamped (valid) addresses and masked afterwards: a
-  // load whose value is consumed inside a divergent branch makes the
-  // compiler wait there for every load issued before it, which would turn
-  // the J blocks into J round trips to memory.
+  // issue every load of this wave first, with no branch: where a branch
+  // around a load joins, the compiler may copy the loaded register, and
+  // that copy waits for every load issued before it, turning the J blocks
+  // into J round trips to memory.  The buffer resources mask the fragments;
+  // the block scales are loaded from clamped (valid) addresses and masked
+  // afterwards.
   v8i wr[J][RW], xr[J][TMX];
   float sab[J][TMX];
   float sar[J][TMX], sbr[J];
@@ -983,13 +984,11 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
   for (int j = 0; j < J; ++j) {
     const int kb = kb0 + WK * j;
     const bool on = kb < KB;
+    const uint32_t koff = on ? static_cast<uint32_t>(kb * kBK) : kOutside;
 #pragma unroll
-    for (int i = 0; i < RW; ++i)
-      wr[j][i] = on ? load_frag_global(wrow[i] + kb * kBK) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < RW; ++i) wr[j][i] = load_frag_buffer(wres, woff[i] + koff);
 #pragma unroll
-    for (int t = 0; t < TMX; ++t)
-      xr[j][t] = (on && xok[t]) ? load_frag_global(xrow[t] + kb * kBK)
-                                : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = 0; t < TMX; ++t) xr[j][t] = load_frag_buffer(xres, xoff[t] + koff);
     if constexpr (BLOCK) {
       const int kbc = on ? kb : KB - 1;
       sbr[j] = sb[sb_row + kbc];
@@ -1000,6 +999,15 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
       }
     }
   }
+  // keep every load above this point: the optimizer otherwise sinks each
+  // block's loads into the branch that uses them (after the test for blocks
+  // past K), and the scheduler toward their first use to save registers,
+  // which again costs one round trip per block.  An empty asm that takes
+  // the operand and scale pointers and clobbers memory stops the former
+  // (with the pointers passed in, it may write what the loads read, so they
+  // cannot move below it); the scheduling barrier stops the latter.
+  asm volatile("" ::"s"(A), "s"(B), "s"(sa), "s"(sb) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (BLOCK) {
 #pragma unroll
     for (int j = 0; j < J; ++j)
@@ -1070,35 +1078,46 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
 }
 
 // Ordered sum of the split-K partials (fp32, or exact int32 for the int8
-// engine), then (scaled_mm) the epilogue scales.
+// engine), then (scaled_mm) the epilogue scales.  The partials of a split
+// are loaded kReduceBatch at a time before any is added (clamped to the last
+// split, the surplus unused), so a thread waits for one memory round trip
+// per batch rather than one per split; the sum still runs in split order.
+constexpr int kReduceBatch = 8;
+
 template <bool BLOCK, bool INT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict__ y,
                                                             const float* __restrict__ ws,
                                                             const float* __restrict__ sa,
                                                             const float* __restrict__ sb,
                                                             int M, int N, int SPLIT) {
+  typedef typename std::conditional<INT, int4, float4>::type V;
   const long total = static_cast<long>(M) * (N / 4);
+  const long plane = static_cast<long>(M) * N;  // floats per split
   for (long idx = blockIdx.x * 256L + threadIdx.x; idx < total; idx += gridDim.x * 256L) {
     const int m = static_cast<int>(idx / (N / 4));
     const int n = static_cast<int>(idx % (N / 4)) * 4;
-    float4 v;
-    if constexpr (INT) {
-      int4 t = *reinterpret_cast<const int4*>(ws + static_cast<long>(m) * N + n);
-      for (int s = 1; s < SPLIT; ++s) {
-        const int4 u =
-            *reinterpret_cast<const int4*>(ws + (static_cast<long>(s) * M + m) * N + n);
-        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    const float* p = ws + static_cast<long>(m) * N + n;
+    V t = *reinterpret_cast<const V*>(p);
+    for (int s0 = 1; s0 < SPLIT; s0 += kReduceBatch) {
+      V u[kReduceBatch];
+#pragma unroll
+      for (int i = 0; i < kReduceBatch; ++i) {
+        const int s = s0 + i < SPLIT ? s0 + i : SPLIT - 1;
+        u[i] = *reinterpret_cast<const V*>(p + s * plane);
       }
-      v = make_float4(static_cast<float>(t.x), static_cast<float>(t.y),
-                      static_cast<float>(t.z), static_cast<float>(t.w));
-    } else {
-      v = *reinterpret_cast<const float4*>(ws + static_cast<long>(m) * N + n);
-      for (int s = 1; s < SPLIT; ++s) {
-        const float4 u =
-            *reinterpret_cast<const float4*>(ws + (static_cast<long>(s) * M + m) * N + n);
-        v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+#pragma unroll
+      for (int i = 0; i < kReduceBatch; ++i) {
+        if (s0 + i < SPLIT) {
+          t.x += u[i].x; t.y += u[i].y; t.z += u[i].z; t.w += u[i].w;
+        }
       }
     }
+    float4 v;
+    if constexpr (INT)
+      v = make_float4(static_cast<float>(t.x), static_cast<float>(t.y),
+                      static_cast<float>(t.z), static_cast<float>(t.w));
+    else
+      v = t;
     if constexpr (!BLOCK) {
       const float sm = sa[m];
       const float4 s4 = *reinterpret_cast<const float4*>(sb + n);
@@ -1377,7 +1396,7 @@ hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const 
   if (split <= 1) return hipSuccess;
   const long total = static_cast<long>(M) * (N / 4);
   long blocks = (total + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 8192) blocks = 8192;
   if (blockwise)
     hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), dim3(blocks), dim3(256), 0, st, y,
                        wsf, sa, sb, M, N, split);

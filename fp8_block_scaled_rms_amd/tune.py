@@ -7,15 +7,20 @@ parameters (page "Helion can accelerate vLLM LLM inference on NVIDIA GPUs",
 aihirek.info, section "Autotuning picks the right variant": the algorithm is
 a tuned parameter chosen per shape instead of a hand-written rule).
 
-    python -m fp8_block_scaled_rms_amd.tune --out results.jsonl [--write-table]
+    python -m fp8_block_scaled_rms_amd.tune --out results.jsonl [--write-table PATH]
         [--engine exact|fp8|all] [--shapes default|quick]
+    python -m fp8_block_scaled_rms_amd.tune --from-results RESULTS --write-table PATH
 
 Results are appended to a JSONL file, one line per (shape, variant), and a
 rerun skips what the file already holds (resumable).  Timing: HIP events
 around a batch of back-to-back launches on the current stream (mean per
-launch); every repetition reads its own copy of the weights, rotating
-through >= 1 GiB of copies, so no run is served by the 256 MB last-level
-cache.
+launch, median of three batches); every repetition reads its own copy of
+the weights, rotating through >= 1 GiB of copies, so no run is served by the
+256 MB last-level cache.
+
+The committed table is a pure function of the committed results file
+(csrc/tune_results.jsonl): --from-results rewrites it without a GPU, byte
+for byte (a CPU test checks that it does).
 """
 from __future__ import annotations
 
@@ -82,6 +87,8 @@ def variants(op, M, N, K, engine):
     return out
 
 
+BATCHES = 3
+
 # GPU clock cycles of the spin kernel that the timed launches queue behind
 # (a few milliseconds, longer than the host needs to issue them)
 QUEUE_AHEAD_CYCLES = 8_000_000
@@ -127,20 +134,53 @@ def time_shape(op, M, N, K, cands, reps=10):
         # kernel: the GPU then runs them without waiting for the host, whose
         # per-call cost through this binding (about 10 us) exceeds a small
         # kernel's duration.  Per-launch events would add their own overhead.
-        torch.cuda.synchronize()
-        torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for r in range(reps):
-            run(bs[r % copies])
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) * 1e3 / reps
+        batches = []
+        for _ in range(BATCHES):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(reps):
+                run(bs[r % copies])
+            e1.record()
+            torch.cuda.synchronize()
+            batches.append(e0.elapsed_time(e1) * 1e3 / reps)
+        res[name] = sorted(batches)[BATCHES // 2]
     return res
 
 
-def write_table(rows, path):
+RESULTS_FILE = os.path.join(HERE, "csrc", "tune_results.jsonl")
+TABLE_FILE = os.path.join(HERE, "csrc", "tune_table.inc")
+
+
+def load_results(path):
+    """{(op, M, N, K, variant): us}; a later line for the same key wins."""
+    done = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                if line.strip():
+                    r = json.loads(line)
+                    done[(r["op"], r["M"], r["N"], r["K"], r["variant"])] = r["us"]
+    return done
+
+
+def exact_choices(done):
+    """Per measured shape, the fastest variant of the engine that meets the
+    GEMM tolerance: f16_ (e4m3 widened exactly to f16) for the FP8 ops, i8_
+    for int8.  The FP8-MFMA engine's (f8_) grouped truncation is outside the
+    tolerance, so its times never pick a table row."""
+    per_shape = {}
+    for (op, M, N, K, name), us in done.items():
+        if name.startswith(("f16_", "i8_")):
+            per_shape.setdefault((op, M, N, K), {})[name] = us
+    # ties go to the name that sorts first, so the choice is a function of the times
+    return [(op, M, N, K, min(sorted(c), key=c.get))
+            for (op, M, N, K), c in sorted(per_shape.items())]
+
+
+def table_text(rows):
     """rows: list of (op, M, N, K, best_name).  One table row per measured M;
     the row's M_max is that M, the largest measured M of a family also
     serves everything above it."""
@@ -151,33 +191,43 @@ def write_table(rows, path):
              "// op 0 = scaled_mm, 1 = scaled_mm_blockwise, 2 = scaled_mm_int8.  For a call",
              "// (op, M, N, K) the first row with the same op, N and K and M <= M_max wins;",
              "// shapes absent from the table use the built-in rule in dispatch.cpp.",
-             "// Written by fp8_block_scaled_rms_amd/tune.py from MI355X measurements."]
+             "// Generated from the MI355X times in tune_results.jsonl (no hand edits):",
+             "//   python -m fp8_block_scaled_rms_amd.tune --from-results \\",
+             "//       fp8_block_scaled_rms_amd/csrc/tune_results.jsonl \\",
+             "//       --write-table fp8_block_scaled_rms_amd/csrc/tune_table.inc"]
     for (op, N, K), ms in sorted(fam.items()):
         ms.sort()
         for j, (M, name) in enumerate(ms):
             m_max = M if j + 1 < len(ms) else 1 << 30
             lines.append(f'{{{op}, {N}, {K}, {m_max}, "{name}"}},')
+    return "\n".join(lines) + "\n"
+
+
+def write_table(rows, path):
     with open(path, "w") as f:
-        f.write("\n".join(lines) + "\n")
+        f.write(table_text(rows))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default="tune_results.jsonl")
     ap.add_argument("--engine", default="exact", choices=["exact", "fp8", "all"])
-    ap.add_argument("--shapes", default="default", choices=["default", "quick", "large", "int8"])
+    ap.add_argument("--shapes", default="default",
+                    choices=["default", "quick", "large", "int8", "small"])
     ap.add_argument("--write-table", default=None, help="path of the table to write")
+    ap.add_argument("--from-results", default=None,
+                    help="write the table from this results file without measuring")
     ap.add_argument("--reps", type=int, default=20)
     args = ap.parse_args()
-    done = {}
-    if os.path.exists(args.out):
-        with open(args.out) as f:
-            for line in f:
-                r = json.loads(line)
-                done[(r["op"], r["M"], r["N"], r["K"], r["variant"])] = r["us"]
+    if args.from_results:
+        if not args.write_table:
+            ap.error("--from-results needs --write-table")
+        write_table(exact_choices(load_results(args.from_results)), args.write_table)
+        return
+    done = load_results(args.out)
     shapes = {"default": SHAPES, "quick": QUICK, "large": LARGE,
-              "int8": [sh for sh in SHAPES if sh[0] == I8]}[args.shapes]
-    best_rows = []
+              "int8": [sh for sh in SHAPES if sh[0] == I8],
+              "small": [sh for sh in SHAPES if sh[0] != I8 and sh[1] <= 128]}[args.shapes]
     with open(args.out, "a") as f:
         for op, M, N, K in shapes:
             cands = variants(op, M, N, K, args.engine)
@@ -191,19 +241,14 @@ def main():
                 f.flush()
             mine = {n: done[(op, M, N, K, n)] for _, n in cands}
             best = min(mine, key=mine.get)
-            # the default table holds exact-engine variants only: the FP8-MFMA
-            # engine's grouped truncation is outside the GEMM tolerance
-            exact = {n: us for n, us in mine.items() if n.startswith(("f16_", "i8_"))}
-            best_exact = min(exact, key=exact.get) if exact else None
             flops = 2.0 * M * N * K
             byts = M * K + N * K + 2 * M * N
             print(f"op{op} M={M:5d} N={N:6d} K={K:6d} best {best:30s} {mine[best]:9.1f}us "
                   f"{flops / mine[best] / 1e6:8.1f}TF {byts / mine[best] / 1e3:7.0f}GB/s "
                   f"({len(mine)} variants)", flush=True)
-            if best_exact:
-                best_rows.append((op, M, N, K, best_exact))
     if args.write_table:
-        write_table(best_rows, args.write_table)
+        # the same function of the results file as --from-results
+        write_table(exact_choices(load_results(args.out)), args.write_table)
 
 
 if __name__ == "__main__":
