@@ -191,10 +191,9 @@ def table_text(rows):
              "// op 0 = scaled_mm, 1 = scaled_mm_blockwise, 2 = scaled_mm_int8.  For a call",
              "// (op, M, N, K) the first row with the same op, N and K and M <= M_max wins;",
              "// shapes absent from the table use the built-in rule in dispatch.cpp.",
-             "// Generated from the MI355X times in tune_results.jsonl (no hand edits):",
-             "//   python -m fp8_block_scaled_rms_amd.tune --from-results \\",
-             "//       fp8_block_scaled_rms_amd/csrc/tune_results.jsonl \\",
-             "//       --write-table fp8_block_scaled_rms_amd/csrc/tune_table.inc"]
+             "// Generated from the MI355X times in tune_results.jsonl (no hand edits) by",
+             "// python -m fp8_block_scaled_rms_amd.tune --from-results RESULTS --write-table",
+             "// TABLE, with RESULTS and TABLE that file and this one (in csrc/)."]
     for (op, N, K), ms in sorted(fam.items()):
         ms.sort()
         for j, (M, name) in enumerate(ms):
