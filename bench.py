@@ -152,6 +152,7 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_32b_prefill_gate_up_m8192.md")
 KERNEL_SOURCES = ("fp8_block_scaled_rms_amd/csrc/gemm_kernels.hip",
                   "fp8_block_scaled_rms_amd/csrc/gemm_kernels.h",
+                  "fp8_block_scaled_rms_amd/csrc/gemm_common.hpp",
                   "fp8_block_scaled_rms_amd/csrc/fp8q_common.hpp",
                   "fp8_block_scaled_rms_amd/csrc/silu_table.hpp")
 

@@ -1172,7 +1172,12 @@ Variant tiled_variant() {
   if constexpr (E != kEngineI8)
     v.fn[1] =
         reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E, PRIO>);
-  if constexpr (E == kEngineF16)
+  // Power-of-two scales are folded into the widening only in the eight-wave
+  // tiles, where that measured faster (the 32B prefill gate_up at M=8192:
+  // 3776 us against 3997 us on the general path).  The four-wave tiles keep
+  // the rotated loop, whose general path measured faster (the 32B qkv at
+  // M=2048 on the 128x128 tile: 186 us against 197 us folded).
+  if constexpr (E == kEngineF16 && WM * WN == 8)
     v.fn[2] = reinterpret_cast<const void*>(
         &gemm_tiled_kernel<BM, BN, WM, WN, ST, true, E, PRIO, true>);
   else

@@ -195,13 +195,15 @@ int fp8q_scaled_mm_int8(void* y, const void* a, const void* b, const float* sa,
 /* ------------------------------------------------------------------------
  * scaled_mm_blockwise for power-of-two (UE8M0) scales, e.g. activations from
  * the FP8Q_GROUP128_UE8M0 quantizer and weights with power-of-two block
- * scales.  Same arguments and result as fp8q_scaled_mm_blockwise.  The tiled
- * kernels fold such scales exactly into the e4m3 -> f16 widening and drop
- * the per-block scale multiply-add (page "Helion in vLLM: FP8 inference of
- * Qwen3", section "Practical limits", on UE8M0 scales); wherever a scale is
- * not a power of two, or the exponents of one token row or weight block
- * span more than 22 binades, those kernels take the general path, so any
- * scales give the fp8q_scaled_mm_blockwise result.
+ * scales.  Same arguments and result as fp8q_scaled_mm_blockwise.  The
+ * eight-wave tiled kernels fold such scales exactly into the e4m3 -> f16
+ * widening and drop the per-block scale multiply-add (page "Helion in vLLM:
+ * FP8 inference of Qwen3", section "Practical limits", on UE8M0 scales);
+ * wherever a scale is not a power of two, or the exponents of one token row
+ * or weight block span more than 22 binades, those kernels take the general
+ * path, so any scales give the fp8q_scaled_mm_blockwise result.  The other
+ * variants (four-wave tiles, the weight-streaming kernel), where folding
+ * measured no faster, run the general path throughout.
  * ---------------------------------------------------------------------- */
 int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const void* b, const float* sa,
                                    const float* sb, int64_t M, int64_t N, int64_t K, void* ws,

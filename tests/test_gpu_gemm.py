@@ -327,12 +327,27 @@ def test_ue8m0_mixed_folding_waves(name):
     assert res["ok"], res
 
 
-def test_ue8m0_falls_back_on_general_or_spread_scales():
-    """Scales that are not powers of two take the general path (same bytes as
-    scaled_mm_blockwise); so do power-of-two scales whose exponents span more
-    than the f16 window, which must still match the oracle."""
+def test_ue8m0_four_wave_tiles_run_the_general_path():
+    """Folding measured slower in the four-wave tiles, so there the UE8M0
+    entry runs the general blockwise kernel: bit for bit its result."""
     M, N, K = 200, 256, 3072
     cfg = next(i for i, n in _configs() if n == "f16_tiled_m128_n128_w2x2_st2")
+    say("ue8m0 four-wave general path", M, N, K)
+    rng = synth.rng_for("ue8-fourwave")
+    a = synth.gen_e4m3_codes(rng, (M, K))
+    b = synth.gen_e4m3_codes(rng, (N, K))
+    sa, sb = _scales(rng, BW, M, N, K, pow2=True)
+    assert torch.equal(_run_ue8(a, sa, b, sb, cfg), _run(BW, a, sa, b, sb, cfg))
+
+
+def test_ue8m0_falls_back_on_general_or_spread_scales():
+    """In a folding (eight-wave) tile, scales that are not powers of two take
+    the general path (same bytes as scaled_mm_blockwise); so do power-of-two
+    scales whose exponents span more than the f16 window, which must still
+    match the oracle."""
+    M, N, K = 200, 256, 3072
+    cfg = next(i for i, n in _configs() if n == "f16_tiled_m128_n256_w2x4_st3")
+    say("ue8m0 fallback", M, N, K)
     rng = synth.rng_for("ue8-fallback")
     a = synth.gen_e4m3_codes(rng, (M, K))
     b = synth.gen_e4m3_codes(rng, (N, K))
