@@ -34,6 +34,7 @@ shapes, and ue8m0_blockwise the prefill GEMMs with power-of-two scales.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --decode-study   small-M GEMMs beside a read-only kernel
                                         streaming the same weight bytes
+       python bench.py --chain-study    the decode chain eagerly and as a graph
 """
 from __future__ import annotations
 
@@ -138,6 +139,9 @@ def parse():
                    help="only time the small-M (HBM-bound) GEMM launches of a step, each beside "
                         "a read-only kernel streaming the same weight bytes, and print that "
                         "comparison as one JSON line")
+    p.add_argument("--chain-study", action="store_true",
+                   help="only run the decode-chain comparison (eager vs HIP graph) and print "
+                        "it as one JSON line, for a kernel trace of the two")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (3 times), the known-size "
                         "reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -807,6 +811,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     step = Step(fq, torch, dev)
+    if args.chain_study:
+        print(json.dumps({"decode_chain": decode_chain_latency(step)}), flush=True)
+        return
     cfg_of = build(step)
     total_flops = sum(c[2] for c in step.calls)
     if args.decode_study:

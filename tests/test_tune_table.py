@@ -33,6 +33,19 @@ def test_table_names_registered_exact_variants():
         assert name.startswith("i8_" if op == tune.I8 else "f16_"), (op, name)
 
 
+def test_noalloc_test_shapes_split_k():
+    """tests/test_zz_no_alloc.py exercises the scratch array on shapes whose
+    table variant splits K; a regenerated table must keep them splitting."""
+    pairs = [((64, 5120, 25600), (32, 4096, 12288)), ((32, 24576, 4096), (16, 4096, 12288))]
+    for pair in pairs:
+        needs = [fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, *s) for s in pair]
+        assert all(n > 0 for n in needs), (pair, needs)
+        assert needs[1] < needs[0], (pair, needs)  # the second call is the smaller
+        assert needs[0] <= 64 << 20
+    big = fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, 2048, 5120, 25600)
+    assert big > 64 << 20  # the oversized case the no-alloc entry rejects
+
+
 def test_choice_is_the_fastest_and_ties_break_by_name():
     done = {(1, 8, 256, 512, "f16_b"): 2.0, (1, 8, 256, 512, "f16_a"): 2.0,
             (1, 8, 256, 512, "f8_c"): 1.0, (1, 16, 256, 512, "f16_b"): 3.0,

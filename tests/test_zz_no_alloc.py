@@ -44,8 +44,12 @@ def _both(M, N, K, tag):
     return y, y_ref, need
 
 
-@pytest.mark.parametrize("first,second", [((64, 5120, 25600), (32, 4096, 12288)),
-                                          ((32, 24576, 4096), (8, 4096, 12288))])
+# split-K shapes under the committed table (tests/test_tune_table.py checks
+# on the CPU that they still split after the table is regenerated)
+SPLIT_PAIRS = [((64, 5120, 25600), (32, 4096, 12288)), ((32, 24576, 4096), (16, 4096, 12288))]
+
+
+@pytest.mark.parametrize("first,second", SPLIT_PAIRS)
 def test_noalloc_matches_workspace_path_twice(first, second):
     for i, (M, N, K) in enumerate((first, second)):
         say("noalloc", i, M, N, K)
