@@ -384,3 +384,37 @@ def test_calls_on_a_side_stream_are_ordered_by_that_stream():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     assert torch.equal(q0, q1) and torch.equal(s0, s1) and torch.equal(y0, y1)
+
+
+def test_rows_past_32bit_byte_offsets():
+    """M*K beyond 2^32 bytes of A (M = 2^20 + 256, K = 4096): the tiled
+    kernels address a tile's token rows with 32-bit offsets from the tile's
+    first row and clamp the last tile's rows, which must not wrap.  Rows on
+    both sides of the 2^32 boundary against the oracle; then the fused
+    SiLU-and-mul epilogue on the same operands against the two-kernel path
+    with the same tile, on every row."""
+    M, N, K = (1 << 20) + 256, 256, 4096
+    say("rows past 2^32 bytes", M, N, K)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242)
+    a = torch.randint(0, 255, (M, K), generator=g, device=DEV, dtype=torch.uint8) & 0xF7
+    b = torch.randint(0, 255, (N, K), generator=g, device=DEV, dtype=torch.uint8) & 0xF7
+    sa = torch.rand((M, K // 128), generator=g, device=DEV) + 0.5
+    sb = torch.rand((N // 128, K // 128), generator=g, device=DEV) + 0.5
+    name = "f16_tiled_m128_n256_w2x4_st3"
+    cfg = next(i for i, n in _configs() if n == name)
+    y = fq.scaled_mm_blockwise(a, b, sa, sb, cfg=cfg)
+    torch.cuda.synchronize()
+    edge = (1 << 32) // K  # first row whose byte offset from A passes 2^32
+    rows = np.array([0, 1, 127, edge - 129, edge - 1, edge, edge + 1, edge + 200, M - 129,
+                     M - 128, M - 2, M - 1])
+    ri = torch.from_numpy(rows).to(DEV)
+    ref = gemm.scaled_mm_blockwise(host(a[ri]), host(sa[ri]), host(b), host(sb))
+    res = gemm.acceptance(bf16_host_f64(y[ri]), ref)
+    assert res["ok"], res
+    q2, s2 = fq.silu_mul_quant(y, fq.GROUP128)
+    del y
+    q1, s1 = fq.scaled_mm_blockwise_silu_quant(a, b, sa, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
