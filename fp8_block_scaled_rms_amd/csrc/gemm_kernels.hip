@@ -1221,6 +1221,10 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 1>());
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineF16, 1>());
     v.push_back(tiled_variant<128, 128, 4, 2, 3, kEngineF16>());
+    // small tiles of four waves: more workgroups for mid-size GEMMs
+    v.push_back(tiled_variant<64, 64, 2, 2, 3, kEngineF16>());
+    v.push_back(tiled_variant<64, 64, 2, 2, 3, kEngineF16, 0, 4>());
+    v.push_back(tiled_variant<64, 128, 2, 2, 3, kEngineF16>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 4>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 16>());
@@ -1277,6 +1281,8 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<128, 256, 2, 4, 3, kEngineI8>());
     v.push_back(tiled_variant<128, 128, 4, 2, 3, kEngineI8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineI8>());
+    v.push_back(tiled_variant<64, 64, 2, 2, 3, kEngineI8>());
+    v.push_back(tiled_variant<64, 128, 2, 2, 3, kEngineI8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineI8, 0, 4>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineI8, 0, 2>());
 #define FP8Q_SKINNY_I8(T, R, W, J) v.push_back(skinny_variant<T, R, W, J, kEngineI8>());

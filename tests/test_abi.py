@@ -147,9 +147,11 @@ def test_noalloc_gemm_argument_checks():
     M, N, K = 2048, 5120, 25600
     assert fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, M, N, K) > 64 << 20
     assert f(A, B, C, D, E, M, N, K, None) == WS
-    # every decode / small-M shape of the workloads fits
-    for M, N, K in ((32, 24576, 4096), (64, 5120, 25600), (32, 4096, 12288)):
-        assert 0 < fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, M, N, K) <= 64 << 20
+    # every decode / small-M blockwise shape of the workloads fits
+    decode = [(M, N, K) for M in (1, 2, 4, 8, 16, 32)
+              for N, K in ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288))]
+    for M, N, K in decode + [(64, 5120, 25600)]:
+        assert fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, M, N, K) <= 64 << 20
 
 
 def test_gemm_k_limit():
