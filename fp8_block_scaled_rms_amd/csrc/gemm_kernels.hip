@@ -1224,7 +1224,10 @@ std::vector<Variant>& registry() {
     // small tiles of four waves: more workgroups for mid-size GEMMs
     v.push_back(tiled_variant<64, 64, 2, 2, 3, kEngineF16>());
     v.push_back(tiled_variant<64, 64, 2, 2, 3, kEngineF16, 0, 4>());
+    v.push_back(tiled_variant<64, 64, 2, 2, 3, kEngineF16, 0, 8>());
+    v.push_back(tiled_variant<64, 64, 2, 2, 3, kEngineF16, 0, 16>());
     v.push_back(tiled_variant<64, 128, 2, 2, 3, kEngineF16>());
+    v.push_back(tiled_variant<64, 128, 2, 2, 3, kEngineF16, 0, 8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 4>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 8>());
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 16>());
