@@ -738,6 +738,81 @@ def ue8m0_gemm(step: Step, reps: int = 6):
     return out
 
 
+def library_context(step: Step, kt, reps: int = 5):
+    """Context from the installed libraries on the same GPU (not part of the
+    path, and not a target): torch's f16 matmul (hipBLASLt) and FP8
+    _scaled_mm with per-tensor scales on the dominant GEMM's shape, which
+    compute neither the blockwise scales nor the exact FP8 sums, and torch
+    eager compositions of two fused quantizers (the pages compare their
+    kernels with the framework's own ops), each against this library's
+    launch of the same work."""
+    torch = step.torch
+    out = {}
+    M, N, K = 8192, 51200, 5120
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    a = step.randn((M, K)).to(torch.float16)
+    bt = step.randn((K, N), 0.02).to(torch.float16)  # [K, N] contiguous: no transposed operand
+    us = timed(lambda: torch.matmul(a, bt))
+    out["torch_matmul_f16_us"] = round(us, 1)
+    out["torch_matmul_f16_tflops"] = round(2.0 * M * N * K / us / 1e6, 1)
+    del a, bt
+    try:
+        a8 = step.randn((M, K)).to(torch.float8_e4m3fn)
+        b8 = (step.randn((N, K), 0.02) * 64).to(torch.float8_e4m3fn)
+        one = torch.ones((), device=step.dev)
+        us = timed(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
+                                            out_dtype=torch.bfloat16))
+        out["torch_scaled_mm_fp8_per_tensor_us"] = round(us, 1)
+        out["torch_scaled_mm_fp8_per_tensor_tflops"] = round(2.0 * M * N * K / us / 1e6, 1)
+        del a8, b8
+    except Exception as e:  # not every build of torch has it for this GPU
+        out["torch_scaled_mm_fp8_per_tensor"] = f"unavailable: {type(e).__name__}"
+    out["this_library_fused_gate_up_us"] = round(
+        kt["qwen3-32b-block-prefill/M8192/gate_up_silu_mul_quant"], 1)
+
+    def rms_group(x, w):
+        xf = x.float()
+        y = xf * torch.rsqrt(xf.pow(2).mean(dim=1, keepdim=True) + 1e-6) * w.float()
+        g = y.view(x.shape[0], -1, 128)
+        s = g.abs().amax(dim=2, keepdim=True) / 448.0
+        return (g / s).to(torch.float8_e4m3fn), s
+
+    def silu_group(gu):
+        D = gu.shape[1] // 2
+        y = torch.nn.functional.silu(gu[:, :D].float()) * gu[:, D:].float()
+        g = y.view(gu.shape[0], -1, 128)
+        s = g.abs().amax(dim=2, keepdim=True) / 448.0
+        return (g / s).to(torch.float8_e4m3fn), s
+
+    x = step.activations(8192, 5120)
+    w = (1.0 + step.randn((5120,), 0.1)).to(torch.bfloat16)
+    us = timed(lambda: rms_group(x, w))
+    out["torch_eager_rmsnorm_group128_quant_M8192_K5120_us"] = round(us, 1)
+    out["this_library_rmsnorm_group128_quant_us"] = round(
+        kt["qwen3-32b-block-prefill/M8192/rmsnorm_quant"], 1)
+    del x
+    gu = (step.randn((4096, 51200), 2.0)).to(torch.bfloat16)
+    us = timed(lambda: silu_group(gu))
+    out["torch_eager_silu_mul_group128_quant_M4096_D25600_us"] = round(us, 1)
+    out["this_library_silu_mul_group128_quant_us"] = round(
+        kt["qwen3-32b-mlp-tail/M4096/silu_mul_quant"], 1)
+    del gu
+    torch.cuda.empty_cache()
+    return out
+
+
 def int8_sweep(step: Step, reps: int = 20):
     """W8A8 INT8 on the Qwen3-1.7B per-token linear shapes: every GEMM shape
     per M, back-to-back launches between two events (queued behind a spin
@@ -911,6 +986,7 @@ def main():
     chain = decode_chain_latency(step)
     w8a8 = int8_sweep(step)
     ue8 = ue8m0_gemm(step)
+    libctx = library_context(step, kt)
 
     cpu = None
     if not args.no_cpu_baseline and dom[2] > 0:
@@ -944,6 +1020,7 @@ def main():
         "decode_chain": chain,
         "w8a8_int8": w8a8,
         "ue8m0_blockwise": ue8,
+        "library_context": libctx,
     }
     if args.detail:
         detail = {label: {"kind": kind, "us": round(kt[label], 2), "flops": flops,
