@@ -23,46 +23,64 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------- quotient y / s --
-// Correctly rounded fp32 quotient y / s given r = RN(1/s), for
-// 2^-76 <= s < 2^126 and |y| <= 449 s.  Markstein's correction (P. Markstein,
-// "Computation of elementary functions on the IBM RISC System/6000
-// processor", IBM J. Res. Dev. 34(1), 1990): one correction step turns the
-// product y*r (within ~2 ulp) into a faithful quotient, and a second step
-// with an exact remainder then yields the correctly rounded quotient.  That
-// holds whenever |y| >= 2^-100 and |y/s| >= 2^-125 (the remainders are then
-// exact); otherwise the result still has the sign of y and magnitude below
-// 2^-22, which is all the e4m3 encoder needs (such quotients encode to +-0).
-// copysign restores the sign of a zero quotient (the correction turns -0
-// into +0).  tests/host/div_check.cpp checks this against IEEE division.
-__host__ __device__ __forceinline__ float div_rn_corrected(float y, float s, float r) {
-  float q0 = y * r;
-  float e0 = fmaf(-q0, s, y);
-  float q1 = fmaf(e0, r, q0);
-  float e1 = fmaf(-q1, s, y);
-  float q2 = fmaf(e1, r, q1);
-  return copysignf(q2, y);
+// The quantizers need RN32(y / s) exactly (IEEE fp32 division) for fp32 y
+// and s > 0.  It is formed from an fp64 product: q = RN32(RN64(y * r)) with
+// r an fp64 reciprocal of s of relative error at most ~2^-52 (here RN64(1/s)).
+// Why that is exact:
+//  * q64 = RN64(y * r) differs from y/s by a relative error below 2^-51.9.
+//  * RN32(q64) != RN32(y/s) needs an fp32 rounding boundary (a midpoint m of
+//    two adjacent fp32 values, a number with a 25-bit odd significand when
+//    y/s >= 2^-126) between q64 and y/s, or at q64.
+//  * y/s is never a midpoint: y = m * s would give y an odd significand of at
+//    least 25 bits.  And it is never close to one: y - m*s is a non-zero
+//    multiple of 2^min(ey, em + es) (ulp exponents of y, m and s), so at
+//    least 2^-24 |y| or 2^-49 |m s|, since y, m and s have at most 24, 25 and
+//    24 significant bits.  So |y/s - m| >= 2^-49 |m|, while |q64 - y/s| <
+//    2^-51.9 |y/s|: no boundary lies between them.
+//  * Quotients below 2^-126 (where fp32 midpoints have fewer bits) keep
+//    their sign and a magnitude below 2^-125; every such quotient encodes to
+//    a signed zero in e4m3 and int8, the only use made of them.
+//  * q64 cannot overflow; a huge quotient converts to +-inf, which the
+//    encoders saturate (only a static scale allows it).
+// Three fp64-unit instructions (widen, multiply, narrow) per element, where
+// a two-step fp32 correction of y * RN32(1/s) takes six.
+// tests/host/div_check.cpp checks it against IEEE division on the host.
+__host__ __device__ __forceinline__ float div_rn_f64(float y, double r) {
+  return static_cast<float>(static_cast<double>(y) * r);
 }
 
-// Scale of a group from its amax, the reciprocal used by the corrected
-// quotient, and whether the fast quotient is valid for that scale.
+// RN32(amax / d) for the scale divisors d = 448 (e4m3) and 127 (int8):
+// the same argument with r = RN64(1/d) (d has 3 and 7 significant bits), for
+// quotients in the normal fp32 range; below it (amax < 2^-100) IEEE division.
+__host__ __device__ __forceinline__ float scale_div(float amax, double recip_d, float d) {
+  if (__builtin_expect(amax >= 0x1p-100f, 1)) return div_rn_f64(amax, recip_d);
+  return amax / d;
+}
+constexpr double kRecip448 = 1.0 / 448.0;  // RN64 (constant-folded IEEE division)
+constexpr double kRecip127 = 1.0 / 127.0;
+
+// Scale of a group and the fp64 reciprocal used by its quotients; a zero
+// scale (all-zero group, or amax below 448 * 2^-150) takes r = 1, so the
+// quotients are the signed zeros (or values below 2^-140) that encode to
+// +-0, as the definition asks of a zero scale.
 struct GroupScale {
   float s;
-  float r;
-  bool fast;
+  double r;
 };
+__host__ __device__ __forceinline__ double recip_or_one(float s) {
+  return s > 0.0f ? 1.0 / static_cast<double>(s) : 1.0;
+}
 __device__ __forceinline__ GroupScale make_scale(float amax) {
   GroupScale g;
-  g.s = amax / kE4M3Max;  // IEEE division (correctly rounded build flags)
-  g.fast = g.s >= 0x1p-76f;
-  g.r = g.fast ? 1.0f / g.s : 1.0f;
+  g.s = scale_div(amax, kRecip448, kE4M3Max);
+  g.r = recip_or_one(g.s);
   return g;
 }
 // Symmetric int8 scale amax / 127 (W8A8 INT8).
 __device__ __forceinline__ GroupScale make_scale_i8(float amax) {
   GroupScale g;
-  g.s = amax / 127.0f;  // IEEE division
-  g.fast = g.s >= 0x1p-76f;
-  g.r = g.fast ? 1.0f / g.s : 1.0f;
+  g.s = scale_div(amax, kRecip127, 127.0f);
+  g.r = recip_or_one(g.s);
   return g;
 }
 
@@ -81,36 +99,21 @@ __device__ __forceinline__ GroupScale make_scale_ue8m0(float amax) {
   }
   GroupScale g;
   g.s = (e >= -126) ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23) : 0x1p-127f;
-  g.fast = g.s >= 0x1p-76f;
-  g.r = g.fast ? 1.0f / g.s : 1.0f;
+  g.r = recip_or_one(g.s);
   return g;
 }
 
-// A caller-given (static) scale s > 0: the fast quotient where its proof
-// holds, IEEE division elsewhere.
+// A caller-given (static) scale s > 0.
 __device__ __forceinline__ GroupScale static_scale(float s) {
   GroupScale g;
   g.s = s;
-  g.fast = s >= 0x1p-76f && s < 0x1p126f;
-  g.r = g.fast ? 1.0f / s : 1.0f;
+  g.r = recip_or_one(s);
   return g;
 }
 
-// y / s rounded to fp32; a zero scale (all-zero group) passes y (a signed
-// zero) through.
+// y / s rounded to fp32 (any scale: dynamic, power of two or static).
 __device__ __forceinline__ float quotient(float y, const GroupScale& g) {
-  if (g.fast) return div_rn_corrected(y, g.s, g.r);
-  return g.s == 0.0f ? y : y / g.s;
-}
-// The same for a static scale, where |y| may exceed 448 s by any factor: y
-// is first clamped to +-449 s (any quotient of magnitude >= 448 encodes to
-// +-448 anyway), which keeps the fast quotient inside its proven range.
-__device__ __forceinline__ float quotient_static(float y, const GroupScale& g) {
-  if (g.fast) {
-    const float lim = 449.0f * g.s;
-    return div_rn_corrected(__builtin_amdgcn_fmed3f(y, -lim, lim), g.s, g.r);
-  }
-  return y / g.s;
+  return div_rn_f64(y, g.r);
 }
 
 // ------------------------------------------------------------- e4m3 --
@@ -140,30 +143,32 @@ __device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d)
 }
 
 // ------------------------------------------------------ reductions --
-// DPP lane moves inside rows of 16 lanes.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
+// DPP controls for lane moves inside rows of 16 lanes.
 constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
 
+// Maxima of amax candidates: non-negative floats (|y| or +0, never NaN or
+// -0), which order as their bit patterns do as unsigned integers.  The
+// integer max needs none of the NaN-quieting moves the compiler adds around
+// a float max of values that come from lane moves.
+__device__ __forceinline__ uint32_t u32_max(uint32_t v, uint32_t w) { return v > w ? v : w; }
 // max over each aligned group of 16 lanes; every lane gets its group's max.
 __device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
-  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
-  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_f32<kDppMirror>(v));
-  return v;
+  uint32_t u = __float_as_uint(v);
+  u = u32_max(u, __builtin_amdgcn_mov_dpp(u, kDppQuadXor1, 0xF, 0xF, false));
+  u = u32_max(u, __builtin_amdgcn_mov_dpp(u, kDppQuadXor2, 0xF, 0xF, false));
+  u = u32_max(u, __builtin_amdgcn_mov_dpp(u, kDppHalfMirror, 0xF, 0xF, false));
+  u = u32_max(u, __builtin_amdgcn_mov_dpp(u, kDppMirror, 0xF, 0xF, false));
+  return __uint_as_float(u);
 }
 // max over the whole wave (all lanes get it).
 __device__ __forceinline__ float max64(float v) {
-  v = max16(v);
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  uint32_t u = __float_as_uint(max16(v));
+  u = u32_max(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 16)));
+  u = u32_max(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 32)));
+  return __uint_as_float(u);
 }
 // fp64 sum over the wave; butterfly order, every lane gets the same value.
 __device__ __forceinline__ double sum64(double v) {

@@ -858,8 +858,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
           cm = fmaxf(cm, fmaxf(fabsf(v[t][h][r]), fabsf(v[t][h][r + 1])));
         }
       // the wave's 32 columns of this token sit in lanes lr, lr + 16, lr + 32, lr + 48
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      {  // non-negative: integer max of the bit patterns (no NaN-quieting moves)
+        uint32_t u = __float_as_uint(cm);
+        u = u32_max(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 16)));
+        u = u32_max(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), 32)));
+        cm = __uint_as_float(u);
+      }
       if (g == 0) red[(wm * S::kTM + 16 * t + lr) * WN + wn] = cm;
     }
     __syncthreads();
@@ -871,7 +875,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       const int m = m0 + row;
       float amax = red[row * WN];
 #pragma unroll
-      for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[row * WN + w]);
+      for (int w = 1; w < WN; ++w)
+        amax = __uint_as_float(u32_max(__float_as_uint(amax), __float_as_uint(red[row * WN + w])));
       if (m >= M) continue;
       const GroupScale gs = make_scale(amax);
       if (wn == 0 && g == 0) ws[static_cast<long>(m) * ngroups + tn] = gs.s;

@@ -210,17 +210,10 @@ void quant_kernel(uint8_t* __restrict__ q,
     auto store_chunk = [&](int i, const float(&yo)[kChunk], const GroupScale& g) {
       const int c = c0 + tid + i * TPR;
       uint2 out;
-      if constexpr (MODE == kStaticTensor) {
-        out.x = pack4<FMT>(quotient_static(yo[0], g), quotient_static(yo[1], g),
-                           quotient_static(yo[2], g), quotient_static(yo[3], g));
-        out.y = pack4<FMT>(quotient_static(yo[4], g), quotient_static(yo[5], g),
-                           quotient_static(yo[6], g), quotient_static(yo[7], g));
-      } else {
-        out.x = pack4<FMT>(quotient(yo[0], g), quotient(yo[1], g), quotient(yo[2], g),
-                           quotient(yo[3], g));
-        out.y = pack4<FMT>(quotient(yo[4], g), quotient(yo[5], g), quotient(yo[6], g),
-                           quotient(yo[7], g));
-      }
+      out.x = pack4<FMT>(quotient(yo[0], g), quotient(yo[1], g), quotient(yo[2], g),
+                         quotient(yo[3], g));
+      out.y = pack4<FMT>(quotient(yo[4], g), quotient(yo[5], g), quotient(yo[6], g),
+                         quotient(yo[7], g));
       *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
     };
 
