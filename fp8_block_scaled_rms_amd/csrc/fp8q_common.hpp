@@ -25,7 +25,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---------------------------------------------------- quotient y / s --
 // The quantizers need RN32(y / s) exactly (IEEE fp32 division) for fp32 y
 // and s > 0.  It is formed from an fp64 product: q = RN32(RN64(y * r)) with
-// r an fp64 reciprocal of s of relative error at most ~2^-52 (here RN64(1/s)).
+// r an fp64 reciprocal of s of relative error at most 2^-53 (1 + 2^-30):
+// RN64(1/s), or the refined reciprocal of recip_refine below.
 // Why that is exact:
 //  * q64 = RN64(y * r) differs from y/s by a relative error below 2^-51.9.
 //  * RN32(q64) != RN32(y/s) needs an fp32 rounding boundary (a midpoint m of
@@ -49,16 +50,6 @@ __host__ __device__ __forceinline__ float div_rn_f64(float y, double r) {
   return static_cast<float>(static_cast<double>(y) * r);
 }
 
-// RN32(amax / d) for the scale divisors d = 448 (e4m3) and 127 (int8):
-// the same argument with r = RN64(1/d) (d has 3 and 7 significant bits), for
-// quotients in the normal fp32 range; below it (amax < 2^-100) IEEE division.
-__host__ __device__ __forceinline__ float scale_div(float amax, double recip_d, float d) {
-  if (__builtin_expect(amax >= 0x1p-100f, 1)) return div_rn_f64(amax, recip_d);
-  return amax / d;
-}
-constexpr double kRecip448 = 1.0 / 448.0;  // RN64 (constant-folded IEEE division)
-constexpr double kRecip127 = 1.0 / 127.0;
-
 // Scale of a group and the fp64 reciprocal used by its quotients; a zero
 // scale (all-zero group, or amax below 448 * 2^-150) takes r = 1, so the
 // quotients are the signed zeros (or values below 2^-140) that encode to
@@ -70,18 +61,52 @@ struct GroupScale {
 __host__ __device__ __forceinline__ double recip_or_one(float s) {
   return s > 0.0f ? 1.0 / static_cast<double>(s) : 1.0;
 }
-__device__ __forceinline__ GroupScale make_scale(float amax) {
+
+// fp64 reciprocal of s from an fp32 seed within 4 ulp of 1/s (the hardware
+// reciprocal is within 1 ulp), by two Newton steps r += r (1 - s r), each
+// with one rounding of the residual and one of the update.  A seed of
+// relative error d0 <= 2^-21 leaves at most d0^2 + 2^-53 (1 + d0) <= 2^-41.9
+// after the first step and 2^-53 (1 + 2^-30) after the second, which keeps
+// the quotient's fp64 product within the 2^-51.9 the exactness argument
+// above needs.  For s in [2^-110, 2^120], where 1/s and the seed are normal
+// fp32 numbers (scales of groups with amax >= 2^-100 lie in [2^-109, 2^120)).
+__host__ __device__ __forceinline__ double recip_refine(float s, float seed) {
+  const double d = s;
+  double r = seed;
+  r = fma(r, fma(-d, r, 1.0), r);
+  r = fma(r, fma(-d, r, 1.0), r);
+  return r;
+}
+__device__ __forceinline__ float rcp_seed(float s) { return __builtin_amdgcn_rcpf(s); }
+
+// Scale s = RN32(amax / d) for d = 448 (e4m3) or 127 (int8) and its
+// reciprocal.  Above amax = 2^-100 (scales of 2^-109 and more, normal
+// quotients): s by the same fp64-product argument with r = RN64(1/d) (d has
+// 3 and 7 significant bits), the reciprocal by recip_refine.  Below: IEEE
+// division and the correctly rounded fp64 reciprocal.
+__host__ __device__ __forceinline__ float scale_div(float amax, double recip_d, float d) {
+  if (__builtin_expect(amax >= 0x1p-100f, 1)) return div_rn_f64(amax, recip_d);
+  return amax / d;
+}
+constexpr double kRecip448 = 1.0 / 448.0;  // RN64 (constant-folded IEEE division)
+constexpr double kRecip127 = 1.0 / 127.0;
+__device__ __forceinline__ GroupScale scale_and_recip(float amax, double recip_d, float d) {
   GroupScale g;
-  g.s = scale_div(amax, kRecip448, kE4M3Max);
-  g.r = recip_or_one(g.s);
+  if (__builtin_expect(amax >= 0x1p-100f, 1)) {
+    g.s = div_rn_f64(amax, recip_d);
+    g.r = recip_refine(g.s, rcp_seed(g.s));
+  } else {
+    g.s = amax / d;
+    g.r = recip_or_one(g.s);
+  }
   return g;
+}
+__device__ __forceinline__ GroupScale make_scale(float amax) {
+  return scale_and_recip(amax, kRecip448, kE4M3Max);
 }
 // Symmetric int8 scale amax / 127 (W8A8 INT8).
 __device__ __forceinline__ GroupScale make_scale_i8(float amax) {
-  GroupScale g;
-  g.s = scale_div(amax, kRecip127, 127.0f);
-  g.r = recip_or_one(g.s);
-  return g;
+  return scale_and_recip(amax, kRecip127, 127.0f);
 }
 
 // Power-of-two (UE8M0) scale: the smallest s = 2^e, e >= -127, with
@@ -125,6 +150,17 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
   c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
   d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return static_cast<uint32_t>(v);
+}
+// The same for quotients by a dynamic scale (amax / 448 rounded, or the
+// power of two at or above it): |v| <= 448 (1 + 2^-23), so no clamp.  The
+// hardware conversion rounds to nearest even over the whole of (448, 464]
+// to +-448 (a NaN code appears only above 464, where no such quotient
+// lies); tests/test_gpu_quant.py checks the amax elements whose quotient is
+// 448 + 2^-15.
+__device__ __forceinline__ uint32_t pack4_e4m3_dynamic(float a, float b, float c, float d) {
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
   return static_cast<uint32_t>(v);

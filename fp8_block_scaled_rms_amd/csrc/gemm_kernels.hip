@@ -884,8 +884,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       for (int h = 0; h < kH; ++h) {
         const int col = o0 + 32 * wn + 16 * h + 4 * g;
         const uint32_t code =
-            pack4_e4m3(quotient(v[t][h][0], gs), quotient(v[t][h][1], gs),
-                       quotient(v[t][h][2], gs), quotient(v[t][h][3], gs));
+            pack4_e4m3_dynamic(quotient(v[t][h][0], gs), quotient(v[t][h][1], gs),
+                               quotient(v[t][h][2], gs), quotient(v[t][h][3], gs));
         *reinterpret_cast<uint32_t*>(q + static_cast<long>(m) * D + col) = code;
       }
     }

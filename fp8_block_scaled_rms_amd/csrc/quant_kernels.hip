@@ -83,10 +83,11 @@ __device__ __forceinline__ float unit_max(float v, float* red) {
 // workgroup (TPR = 128 / 256: long rows, or few rows; cross-wave reductions
 // go through LDS).  Thread t of a unit owns the 8-element chunks t, t + TPR,
 // ..., CH of them.
-template <int FMT>
+template <int FMT, int MODE>
 __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
   if constexpr (FMT == kFmtI8) return pack4_i8(a, b, c, d);
-  return pack4_e4m3(a, b, c, d);
+  if constexpr (MODE == kStaticTensor) return pack4_e4m3(a, b, c, d);  // may exceed 448
+  return pack4_e4m3_dynamic(a, b, c, d);
 }
 
 // Waves per SIMD the register allocation must leave room for: streaming
@@ -210,10 +211,10 @@ void quant_kernel(uint8_t* __restrict__ q,
     auto store_chunk = [&](int i, const float(&yo)[kChunk], const GroupScale& g) {
       const int c = c0 + tid + i * TPR;
       uint2 out;
-      out.x = pack4<FMT>(quotient(yo[0], g), quotient(yo[1], g), quotient(yo[2], g),
-                         quotient(yo[3], g));
-      out.y = pack4<FMT>(quotient(yo[4], g), quotient(yo[5], g), quotient(yo[6], g),
-                         quotient(yo[7], g));
+      out.x = pack4<FMT, MODE>(quotient(yo[0], g), quotient(yo[1], g), quotient(yo[2], g),
+                               quotient(yo[3], g));
+      out.y = pack4<FMT, MODE>(quotient(yo[4], g), quotient(yo[5], g), quotient(yo[6], g),
+                               quotient(yo[7], g));
       *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
     };
 
@@ -250,7 +251,8 @@ void quant_kernel(uint8_t* __restrict__ q,
         if (!valid[i]) continue;
         const int c = c0 + tid + i * TPR;
         const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
-        if ((tid & 15) == 0) scale[static_cast<long>(row) * ngroups + c / 16] = g.s;
+        const long si = static_cast<long>(row) * ngroups + (static_cast<unsigned>(c) >> 4);
+        if ((tid & 15) == 0) scale[si] = g.s;
         store_chunk(i, yo, g);
       }
     } else {  // kStaticTensor: the caller's scale, read once per unit

@@ -1,8 +1,11 @@
 // Host-side check of the library's quotient routines (fp8q_common.hpp:
-// div_rn_f64 with recip_or_one, and scale_div) against IEEE fp32 division,
-// bit for bit.  The device runs the same arithmetic (fp64 multiply of the
-// widened fp32 value, RNE narrowing to fp32, fp64 reciprocal), so agreement
-// here shows the method, not just this compiler, is right.
+// div_rn_f64 with the reciprocals recip_or_one and recip_refine, and
+// scale_div) against IEEE fp32 division, bit for bit.  The device runs the
+// same arithmetic (fp64 multiply of the widened fp32 value, RNE narrowing to
+// fp32, fp64 Newton steps), so agreement here shows the method, not just this
+// compiler, is right.  The device seeds recip_refine with the hardware fp32
+// reciprocal (within 1 ulp); here every seed from 4 ulp below to 4 ulp above
+// RN32(1/s) is tried.
 //
 // Quotients y / s: for each scale s in a list (random, structured, range
 // ends, subnormal), every fp32 y of several binades (all 2^23 significands),
@@ -73,16 +76,27 @@ int main(int argc, char** argv) {
     scales.push_back(s);
   }
   for (float s : scales) {
-    const double r = fp8q::recip_or_one(s);
+    // the reciprocals the library may use for this s: the correctly rounded
+    // one, and where the scale path refines a seed, every seed within 4 ulp
+    std::vector<double> rs = {fp8q::recip_or_one(s)};
+    const bool refined = s >= 0x1p-110f && s <= 0x1p120f;
+    if (refined) {
+      const uint32_t c = bits(1.0f / s);
+      for (int k = -4; k <= 4; ++k) rs.push_back(fp8q::recip_refine(s, from_bits(c + k)));
+    }
     const int es = std::ilogb(s);
-    // exhaustive significands for y in three binades near the top of the range
+    // exhaustive significands for y in three binades near the top of the
+    // range, with the correctly rounded reciprocal and the extreme seeds
     for (int de = 6; de <= 8; ++de) {
       const int ey = es + de;
       if (ey > 127 || ey < -126) continue;
       for (uint32_t m = 0; m < (1u << 23); ++m) {
         const float y = std::ldexp(from_bits(0x3F800000u | m), ey);
-        check_quotient(y, s, r);
-        check_quotient(-y, s, r);
+        for (size_t j : {0, 1, 5, 9}) {  // correctly rounded; seeds -4, 0 and +4 ulp
+          if (j >= rs.size()) break;
+          check_quotient(y, s, rs[j]);
+          check_quotient(-y, s, rs[j]);
+        }
       }
     }
     // random y of any magnitude up to 2^20 * 449 s (static scales allow
@@ -93,9 +107,10 @@ int main(int argc, char** argv) {
       float y = std::exp2(static_cast<float>(uy(rng))) * (rng() & 1 ? -1.0f : 1.0f);
       if (std::fabs(y) >= 0x1p-126f) y = from_bits((bits(y) & 0xFF800000u) | (rng() & 0x7FFFFFu));
       if (std::isinf(y / s)) continue;  // fp32 overflow: both sides saturate in the encoder
-      check_quotient(y, s, r);
+      check_quotient(y, s, rs[rng() % rs.size()]);
     }
-    for (float y : {0.0f, -0.0f}) check_quotient(y, s, r);
+    for (double r : rs)
+      for (float y : {0.0f, -0.0f}) check_quotient(y, s, r);
   }
   // scales: every amax of a few binades, the fallback boundary, random over
   // the whole range, subnormals included

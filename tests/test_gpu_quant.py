@@ -202,6 +202,44 @@ def test_standalone_quant_parity(mode):
     assert np.array_equal(host(s).view(np.uint32), sr.view(np.uint32))
 
 
+def _amax_over_448(lo=0x4000, hi=0x4380):
+    """bf16 magnitudes a whose quotient RN32(a / RN32(a / 448)) is above 448
+    (448 + 2^-15): the largest quotient a dynamic scale produces."""
+    u = np.arange(lo, hi, dtype=np.uint32)
+    a = (u << 16).view(np.float32)
+    s = (a / np.float32(448)).astype(np.float32)
+    return u[(a / s).astype(np.float32) > np.float32(448)].astype(np.uint16)
+
+
+@pytest.mark.parametrize("mode", [fq.PER_TOKEN, fq.GROUP128])
+def test_dynamic_quotient_above_448(mode):
+    """The dynamic-scale encoders convert without a clamp: their quotients are
+    at most 448 + 2^-15, which must encode to +-448.  Every group (or row)
+    maximum here is such a value, of either sign."""
+    M, K = 64, 4096
+    say("quotient above 448", M, K, mode)
+    cand = _amax_over_448()
+    assert cand.size > 50
+    rng = np.random.default_rng(448)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * 0.25)
+    n_unit = K // 128 if mode == fq.GROUP128 else 1
+    width = K // n_unit
+    for m in range(M):
+        for g in range(n_unit):
+            col = g * width + int(rng.integers(width))
+            sign = np.uint16(0x8000) if (m + g) % 2 else np.uint16(0)
+            x[m, col] = cand[(m * n_unit + g) % cand.size] | sign
+    q, s = fq.quant(bf16_dev(x), mode)
+    torch.cuda.synchronize()
+    qr, sr = quant.quantize(x, mode)
+    assert np.array_equal(host(q), qr)
+    assert np.array_equal(host(s).view(np.uint32), sr.view(np.uint32))
+    # every unit's maximum had a quotient above 448 (checked in numpy fp32)
+    y = (x.astype(np.uint32) << 16).view(np.float32).reshape(M, n_unit, width)
+    qf = (y / sr.reshape(M, n_unit, 1)).astype(np.float32)
+    assert int(np.count_nonzero(np.abs(qf) > np.float32(448))) == M * n_unit
+
+
 def test_silu_exhaustive_all_bf16_gates():
     """Every one of the 65 536 bf16 gates (NaN patterns excluded) against the
     oracle's correctly rounded table."""
