@@ -9,6 +9,20 @@ namespace fp8q {
 constexpr float kE4M3Max = 448.0f;
 constexpr int kGroup = 128;  // 1x128 activation groups, 128x128 weight blocks
 
+// ------------------------------------------------------ buffer loads --
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw loads from [base, base + bytes) (bytes < 2^32).
+// A load whose offset lies outside that range returns zeros and reads no
+// memory, so a resource doubles as a branch-free mask.  Word 3 is the gfx9
+// family's raw buffer format (32-bit data format, no swizzle, no thread-id
+// offset).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bit_cast_u4(v4u v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+
 // ---------------------------------------------------------------- bf16 --
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }

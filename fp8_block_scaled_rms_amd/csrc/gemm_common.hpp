@@ -32,18 +32,6 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* y, float a, float b, floa
   *reinterpret_cast<uint2*>(y) = v;
 }
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-// Buffer resource for raw loads from [base, base + bytes) (bytes < 2^32).
-// A load whose offset lies outside that range returns zeros and reads no
-// memory, so a resource doubles as a branch-free mask.  Word 3 is the gfx9
-// family's raw buffer format (32-bit data format, no swizzle, no thread-id
-// offset).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
 // 32 bytes at byte offset `off` of a buffer as one fragment (two 16-byte
 // loads); zeros where the offset is outside the buffer.
 __device__ __forceinline__ v8i load_frag_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {

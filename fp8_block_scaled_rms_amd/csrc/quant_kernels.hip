@@ -90,27 +90,220 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
   return pack4_e4m3_dynamic(a, b, c, d);
 }
 
-// Waves per SIMD the register allocation must leave room for: streaming
-// needs many waves in flight, which the scheduler otherwise trades for
-// instruction-level parallelism across chunks (6 waves: <= 85 VGPRs).
-template <int CH>
-constexpr int quant_waves() { return CH <= 6 ? 6 : 2; }
+// Whether a front end's kernel prefetches its next work unit (see
+// quant_kernel): RMSNorm, whose arithmetic per element is the largest.  The
+// SiLU front end keeps gate, up and (per token) every product live, which
+// leaves no registers for a second unit; the identity front end measured
+// faster with more waves than a prefetching launch keeps.
+constexpr bool quant_prefetch(int op) { return op == kRms; }
+// Waves per compute unit a prefetching launch is sized for (at most).
+constexpr int kPrefetchWavesPerCu = 12;
 
+// A work unit's place: its row, its first chunk and its end chunk; units past
+// the end are inactive (they take part in the barriers, with no loads or
+// stores).
+struct UnitPos {
+  int row, c0, c_end;
+  bool active;
+};
+
+// Loads of a unit.  SiLU-and-mul and RMSNorm read through buffer resources
+// over the unit's own row: chunks at or past the row's end, and every chunk
+// of an inactive unit (a resource of zero bytes), read as zeros without
+// touching memory, so no load sits behind a branch.  (Where a branch around
+// a load joins, the compiler copies the loaded register and the copy waits
+// for every load in flight, which would also wait for a prefetched unit.)
+// The identity front end issues plain 16-byte loads under the chunk's
+// validity, which measured faster for it; an invalid chunk reads as zeros.
+template <int OP, int TPR, int CH>
+__device__ __forceinline__ void load_unit(const UnitPos& p, const uint16_t* x, long in_stride,
+                                          int K, int tid, uint4 (&xv)[CH], uint4 (&wv)[CH]) {
+  const uint16_t* xr = x + static_cast<long>(p.row) * in_stride;
+  if constexpr (OP != kIdent) {
+    const uint32_t row_bytes = p.active ? static_cast<uint32_t>(K) * 2u : 0u;
+    const auto rx = buffer_rsrc(xr, row_bytes);
+    const auto ru = buffer_rsrc(xr + K, OP == kSilu ? row_bytes : 0u);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int off = (p.c0 + tid + i * TPR) * 16;
+      xv[i] = bit_cast_u4(__builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+      if constexpr (OP == kSilu)
+        wv[i] = bit_cast_u4(__builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, 0));  // up
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = p.c0 + tid + i * TPR;
+      xv[i] = (p.active && c < p.c_end) ? *reinterpret_cast<const uint4*>(xr + c * kChunk)
+                                        : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// The RMSNorm weight chunks of a whole-row unit (the same for every row).
+template <int TPR, int CH>
+__device__ __forceinline__ void load_weight(const uint16_t* w, int K, int tid, uint4 (&wv)[CH]) {
+  const auto rw = buffer_rsrc(w, static_cast<uint32_t>(K) * 2u);
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    wv[i] = bit_cast_u4(__builtin_amdgcn_raw_buffer_load_b128(rw, (tid + i * TPR) * 16, 0, 0));
+}
+
+// One work unit, from its loaded chunks to its codes and scales.
+template <int OP, int MODE, int TPR, int CH, int FMT>
+__device__ __forceinline__ void process_unit(const UnitPos& p, const uint4 (&xv)[CH],
+                                             const uint4 (&wv)[CH], uint8_t* __restrict__ q,
+                                             float* __restrict__ scale, int K, float eps,
+                                             int tid, const float* silu_tab, double* red64,
+                                             float* red32) {
+  const int row = p.row, c0 = p.c0, c_end = p.c_end;
+  bool valid[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) valid[i] = p.active && c0 + tid + i * TPR < c_end;
+
+  // ---- RMSNorm: fp64 sum of squares over the row, then the inverse RMS
+  float inv = 1.0f;
+  if constexpr (OP == kRms) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double d0 = bf16_lo(vv[j]), d1 = bf16_hi(vv[j]);
+        ss = fma(d0, d0, ss);
+        ss = fma(d1, d1, ss);
+      }
+    }
+    const double tot = unit_sum<TPR>(ss, red64);
+    const double t = tot / static_cast<double>(K) + static_cast<double>(eps);
+    inv = static_cast<float>(1.0 / sqrt(t));
+  }
+
+  // ---- y (fp32) of chunk i.  SiLU-and-mul in a per-token mode needs every
+  // y twice (for the row's amax, then for the quotients) and keeps them;
+  // every other case forms a chunk's y where it is used, from the raw bf16
+  // registers, with the same operations in the same order (for RMSNorm
+  // RN32(RN32(x * w) * inv), x * w exact), keeping 8 fewer registers live
+  // per chunk.
+  constexpr bool kKeepY = (OP == kSilu) && !mode_is_group(MODE);
+  auto form_y = [&](int i, float(&yo)[kChunk]) {
+    const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+    const uint32_t ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (OP == kIdent) {
+        yo[2 * j] = bf16_lo(vv[j]);
+        yo[2 * j + 1] = bf16_hi(vv[j]);
+      } else if constexpr (OP == kRms) {
+        yo[2 * j] = (bf16_lo(vv[j]) * bf16_lo(ww[j])) * inv;  // x * w exact in fp32
+        yo[2 * j + 1] = (bf16_hi(vv[j]) * bf16_hi(ww[j])) * inv;
+      } else {  // kSilu: gate in xv, up in wv
+        yo[2 * j] = silu_bf16(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(ww[j]);
+        yo[2 * j + 1] = silu_bf16(vv[j] >> 16, silu_tab) * bf16_hi(ww[j]);
+      }
+    }
+  };
+  float ykeep[kKeepY ? CH : 1][kChunk];
+  if constexpr (kKeepY) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) form_y(i, ykeep[i]);
+  }
+  auto chunk_y = [&](int i, float(&yo)[kChunk]) {
+    if constexpr (kKeepY) {
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) yo[j] = ykeep[i][j];
+    } else {
+      form_y(i, yo);
+    }
+  };
+  auto chunk_amax = [&](const float(&yo)[kChunk]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) m = fmaxf(m, fabsf(yo[j]));
+    return m;
+  };
+  auto store_chunk = [&](int i, const float(&yo)[kChunk], const GroupScale& g) {
+    const int c = c0 + tid + i * TPR;
+    uint2 out;
+    out.x = pack4<FMT, MODE>(quotient(yo[0], g), quotient(yo[1], g), quotient(yo[2], g),
+                             quotient(yo[3], g));
+    out.y = pack4<FMT, MODE>(quotient(yo[4], g), quotient(yo[5], g), quotient(yo[6], g),
+                             quotient(yo[7], g));
+    *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
+  };
+
+  if constexpr (mode_is_row(MODE)) {
+    // amax over the row, then the quotients
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (!valid[i]) continue;
+      float yo[kChunk];
+      chunk_y(i, yo);
+      m = fmaxf(m, chunk_amax(yo));
+    }
+    const float amax = unit_max<TPR>(m, red32);
+    const GroupScale g = FMT == kFmtI8      ? make_scale_i8(amax)
+                         : mode_is_ue8(MODE) ? make_scale_ue8m0(amax)
+                                             : make_scale(amax);
+    if (p.active && tid == 0) scale[row] = g.s;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (!valid[i]) continue;
+      float yo[kChunk];
+      chunk_y(i, yo);
+      store_chunk(i, yo, g);
+    }
+  } else if constexpr (mode_is_group(MODE)) {
+    // one 128-group per chunk and 16 lanes: its amax, scale and codes
+    const int ngroups = K / kGroup;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      float yo[kChunk];
+      chunk_y(i, yo);
+      const float amax = max16(valid[i] ? chunk_amax(yo) : 0.0f);  // all 16 lanes agree
+      if (!valid[i]) continue;
+      const int c = c0 + tid + i * TPR;
+      const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
+      const long si = static_cast<long>(row) * ngroups + (static_cast<unsigned>(c) >> 4);
+      if ((tid & 15) == 0) scale[si] = g.s;
+      store_chunk(i, yo, g);
+    }
+  } else {  // kStaticTensor: the caller's scale, read once per unit
+    const GroupScale g = static_scale(scale[0]);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (!valid[i]) continue;
+      float yo[kChunk];
+      chunk_y(i, yo);
+      store_chunk(i, yo, g);
+    }
+  }
+}
+
+// The quantizer kernel.  Workgroups loop over work units (grid-stride); with
+// quant_prefetch(OP) a wave issues the loads of its next unit before it
+// processes the current one (two register sets, the loop unrolled by two so
+// that no loaded register is ever copied), so loads and arithmetic overlap
+// inside each wave even when every unit of the launch is resident at once;
+// RMSNorm then reads its weight row once per wave (every unit of a wave
+// covers the same columns).
 template <int OP, int MODE, int TPR, int CH, int FMT>
 __global__ __launch_bounds__(kThreads)
-void quant_kernel(uint8_t* __restrict__ q,
-                                                         float* __restrict__ scale,
-                                                         const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ w, int M,
-                                                         int K, float eps) {
+void quant_kernel(uint8_t* __restrict__ q, float* __restrict__ scale,
+                  const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int K,
+                  float eps) {
   static_assert(TPR == 64 || TPR == 128 || TPR == kThreads, "unit = 1, 2 or 4 waves");
   constexpr int kUnitsPerBlock = kThreads / TPR;
+  constexpr bool kPrefetch = quant_prefetch(OP);
   __shared__ double red64[4];
   __shared__ float red32[4];
   extern __shared__ float silu_tab[];
   if constexpr (OP == kSilu) load_silu_table(silu_tab);
 
-  const int sub = static_cast<int>(threadIdx.x) / TPR;
+  // the unit index within the workgroup is uniform over a wave
+  const int sub = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / TPR);
   const int tid = static_cast<int>(threadIdx.x) % TPR;
   const int nchunk = K / kChunk;  // chunks per row
   constexpr bool kWholeRow = mode_is_row(MODE) || (OP == kRms);
@@ -119,151 +312,48 @@ void quant_kernel(uint8_t* __restrict__ q,
   const long units = static_cast<long>(M) * nseg;
   const long in_stride = (OP == kSilu) ? 2L * K : K;  // elements per input row
 
-  for (long ub = blockIdx.x; ub * kUnitsPerBlock < units; ub += gridDim.x) {
-    // a unit past the end still takes part in the barriers, with no loads or
-    // stores
+  auto pos = [&](long ub) {
     const long unit_raw = ub * kUnitsPerBlock + sub;
-    const bool active = unit_raw < units;
-    const long unit = active ? unit_raw : 0;
-    const int row = static_cast<int>(unit / nseg);
+    UnitPos p;
+    p.active = unit_raw < units;
+    const long unit = p.active ? unit_raw : 0;
+    p.row = static_cast<int>(unit / nseg);
     const int seg = static_cast<int>(unit % nseg);
-    const int c0 = seg * unit_chunks;  // first chunk of this unit
-    const int c_end = (c0 + unit_chunks < nchunk) ? c0 + unit_chunks : nchunk;
-    const uint16_t* xr = x + row * in_stride;
+    p.c0 = seg * unit_chunks;
+    p.c_end = (p.c0 + unit_chunks < nchunk) ? p.c0 + unit_chunks : nchunk;
+    return p;
+  };
 
-    // ---- load (all chunks first): x (or the gate), and w (or the up half)
-    uint4 xv[CH], wv[CH];
-    bool valid[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = c0 + tid + i * TPR;
-      valid[i] = active && c < c_end;
-      xv[i] = valid[i] ? *reinterpret_cast<const uint4*>(xr + c * kChunk) : make_uint4(0, 0, 0, 0);
-      if constexpr (OP == kRms)
-        wv[i] = valid[i] ? *reinterpret_cast<const uint4*>(w + c * kChunk) : make_uint4(0, 0, 0, 0);
-      if constexpr (OP == kSilu)
-        wv[i] = valid[i] ? *reinterpret_cast<const uint4*>(xr + K + c * kChunk)
-                         : make_uint4(0, 0, 0, 0);  // up
-      if constexpr (OP == kIdent) wv[i] = make_uint4(0, 0, 0, 0);  // unused
+  if constexpr (!kPrefetch) {
+    for (long ub = blockIdx.x; ub * kUnitsPerBlock < units; ub += gridDim.x) {
+      const UnitPos p = pos(ub);
+      uint4 xv[CH], wv[CH];
+      if constexpr (OP == kRms) load_weight<TPR, CH>(w, K, tid, wv);
+      load_unit<OP, TPR, CH>(p, x, in_stride, K, tid, xv, wv);
+      process_unit<OP, MODE, TPR, CH, FMT>(p, xv, wv, q, scale, K, eps, tid, silu_tab, red64,
+                                           red32);
     }
-    // ---- RMSNorm: fp64 sum of squares over the row, then the inverse RMS
-    float inv = 1.0f;
-    if constexpr (OP == kRms) {
-      double ss = 0.0;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const double d0 = bf16_lo(vv[j]), d1 = bf16_hi(vv[j]);
-          ss = fma(d0, d0, ss);
-          ss = fma(d1, d1, ss);
-        }
-      }
-      const double tot = unit_sum<TPR>(ss, red64);
-      const double t = tot / static_cast<double>(K) + static_cast<double>(eps);
-      inv = static_cast<float>(1.0 / sqrt(t));
-    }
-
-    // ---- y (fp32) of chunk i.  SiLU-and-mul in a per-token mode needs every
-    // y twice (for the row's amax, then for the quotients) and keeps them;
-    // every other case forms a chunk's y where it is used, from the raw bf16
-    // registers, with the same operations in the same order (for RMSNorm
-    // RN32(RN32(x * w) * inv), x * w exact), keeping 8 fewer registers live
-    // per chunk.
-    constexpr bool kKeepY = (OP == kSilu) && !mode_is_group(MODE);
-    auto form_y = [&](int i, float(&yo)[kChunk]) {
-      const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-      const uint32_t ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (OP == kIdent) {
-          yo[2 * j] = bf16_lo(vv[j]);
-          yo[2 * j + 1] = bf16_hi(vv[j]);
-        } else if constexpr (OP == kRms) {
-          yo[2 * j] = (bf16_lo(vv[j]) * bf16_lo(ww[j])) * inv;  // x * w exact in fp32
-          yo[2 * j + 1] = (bf16_hi(vv[j]) * bf16_hi(ww[j])) * inv;
-        } else {  // kSilu: gate in xv, up in wv
-          yo[2 * j] = silu_bf16(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(ww[j]);
-          yo[2 * j + 1] = silu_bf16(vv[j] >> 16, silu_tab) * bf16_hi(ww[j]);
-        }
-      }
-    };
-    float ykeep[kKeepY ? CH : 1][kChunk];
-    if constexpr (kKeepY) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) form_y(i, ykeep[i]);
-    }
-    auto chunk_y = [&](int i, float(&yo)[kChunk]) {
-      if constexpr (kKeepY) {
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) yo[j] = ykeep[i][j];
-      } else {
-        form_y(i, yo);
-      }
-    };
-    auto chunk_amax = [&](const float(&yo)[kChunk]) {
-      float m = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) m = fmaxf(m, fabsf(yo[j]));
-      return m;
-    };
-    auto store_chunk = [&](int i, const float(&yo)[kChunk], const GroupScale& g) {
-      const int c = c0 + tid + i * TPR;
-      uint2 out;
-      out.x = pack4<FMT, MODE>(quotient(yo[0], g), quotient(yo[1], g), quotient(yo[2], g),
-                               quotient(yo[3], g));
-      out.y = pack4<FMT, MODE>(quotient(yo[4], g), quotient(yo[5], g), quotient(yo[6], g),
-                               quotient(yo[7], g));
-      *reinterpret_cast<uint2*>(q + static_cast<long>(row) * K + c * kChunk) = out;
-    };
-
-    if constexpr (mode_is_row(MODE)) {
-      // amax over the row, then the quotients
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (!valid[i]) continue;
-        float yo[kChunk];
-        chunk_y(i, yo);
-        m = fmaxf(m, chunk_amax(yo));
-      }
-      const float amax = unit_max<TPR>(m, red32);
-      const GroupScale g = FMT == kFmtI8      ? make_scale_i8(amax)
-                           : mode_is_ue8(MODE) ? make_scale_ue8m0(amax)
-                                               : make_scale(amax);
-      if (active && tid == 0) scale[row] = g.s;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (!valid[i]) continue;
-        float yo[kChunk];
-        chunk_y(i, yo);
-        store_chunk(i, yo, g);
-      }
-    } else if constexpr (mode_is_group(MODE)) {
-      // one 128-group per chunk and 16 lanes: its amax, scale and codes
-      const int ngroups = K / kGroup;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        float yo[kChunk];
-        chunk_y(i, yo);
-        const float amax = max16(valid[i] ? chunk_amax(yo) : 0.0f);  // all 16 lanes agree
-        if (!valid[i]) continue;
-        const int c = c0 + tid + i * TPR;
-        const GroupScale g = mode_is_ue8(MODE) ? make_scale_ue8m0(amax) : make_scale(amax);
-        const long si = static_cast<long>(row) * ngroups + (static_cast<unsigned>(c) >> 4);
-        if ((tid & 15) == 0) scale[si] = g.s;
-        store_chunk(i, yo, g);
-      }
-    } else {  // kStaticTensor: the caller's scale, read once per unit
-      const GroupScale g = static_scale(scale[0]);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (!valid[i]) continue;
-        float yo[kChunk];
-        chunk_y(i, yo);
-        store_chunk(i, yo, g);
-      }
+  } else {
+    long ub = blockIdx.x;
+    if (ub * kUnitsPerBlock >= units) return;  // uniform over the workgroup
+    uint4 wv[CH];
+    if constexpr (OP == kRms) load_weight<TPR, CH>(w, K, tid, wv);
+    uint4 xa[CH], xb[CH];
+    UnitPos pa = pos(ub), pb;
+    load_unit<OP, TPR, CH>(pa, x, in_stride, K, tid, xa, wv);
+    while (true) {
+      pb = pos(ub + gridDim.x);
+      load_unit<OP, TPR, CH>(pb, x, in_stride, K, tid, xb, wv);
+      process_unit<OP, MODE, TPR, CH, FMT>(pa, xa, wv, q, scale, K, eps, tid, silu_tab, red64,
+                                           red32);
+      ub += gridDim.x;
+      if (ub * kUnitsPerBlock >= units) break;
+      pa = pos(ub + gridDim.x);
+      load_unit<OP, TPR, CH>(pa, x, in_stride, K, tid, xa, wv);
+      process_unit<OP, MODE, TPR, CH, FMT>(pb, xb, wv, q, scale, K, eps, tid, silu_tab, red64,
+                                           red32);
+      ub += gridDim.x;
+      if (ub * kUnitsPerBlock >= units) break;
     }
   }
 }
@@ -408,8 +498,13 @@ bool quant_launch_config(int op, int mode, long M, int K, int num_cus, QuantLaun
   if (ch < 0) return false;
   const long units = static_cast<long>(M) * ((nchunk + unit_chunks - 1) / unit_chunks);
   const long blocks = (units + (kThreads / tpr) - 1) / (kThreads / tpr);
-  // the SiLU table costs 32 KiB of LDS fill per workgroup: fewer, looping ones
-  const long cap = static_cast<long>(num_cus) * (op == kSilu ? 4 : 16);
+  // the SiLU table costs 32 KiB of LDS fill per workgroup: fewer, looping
+  // ones; prefetching kernels want several units per wave, so that each
+  // wave's loads of the next unit overlap its arithmetic on the current one
+  const int blocks_per_cu = quant_prefetch(op) ? kPrefetchWavesPerCu / (kThreads / 64)
+                           : op == kSilu       ? 4
+                                               : 16;
+  const long cap = static_cast<long>(num_cus) * blocks_per_cu;
   out->tpr = tpr;
   out->ch = ch;
   out->grid = static_cast<int>(blocks < cap ? blocks : cap);
