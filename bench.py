@@ -498,6 +498,57 @@ def per_kernel_times(step: Step, batches: int = 3):
     return out
 
 
+def size_matched_probes(step: Step, launches, batches: int = 3):
+    """For each (label, is_gemm, nbytes): the streaming probe
+    (include/fp8q_probe.h) moving the same bytes, timed like
+    per_kernel_times (100 back-to-back launches behind a spin kernel, source
+    and destination rotating over 1 GiB and 512 MiB, median of `batches`).
+    A GEMM launch gets the read-only loop over its byte count; a quantizer
+    the copy loop moving the same total (half read, half written, where the
+    quantizer reads two to four bytes per byte it writes).  Small launches
+    carry the fixed costs of starting and draining a kernel, which these
+    probes pay too: the ratio is the launch's distance from a plain stream
+    of its own size."""
+    torch, L = step.torch, step.lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 8 * cus
+    src_pool = 1 << 30
+    dst_pool = 1 << 29
+    src = torch.ones(src_pool, dtype=torch.uint8, device=step.dev)
+    dst = torch.empty(dst_pool, dtype=torch.uint8, device=step.dev)
+    scratch = torch.empty(wgs * 256 * 4, dtype=torch.uint8, device=step.dev)
+    reps = 100
+    out = {}
+    for label, is_gemm, nbytes in launches:
+        kind = 2 if is_gemm else 3
+        n = (int(nbytes if is_gemm else nbytes // 2) // 4096) * 4096
+        nsrc = max(1, src_pool // n)
+        ndst = max(1, dst_pool // n)
+
+        def run(r):
+            d = scratch.data_ptr() if is_gemm else dst.data_ptr() + (r % ndst) * n
+            rc = L.fp8q_probe_stream(kind, src.data_ptr() + (r % nsrc) * n, d, n, wgs,
+                                     step.stream)
+            if rc != 0:
+                raise RuntimeError(f"probe_stream status {rc}")
+
+        run(0)
+        times = []
+        for _ in range(batches):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            queue_ahead(torch, 2_000_000 + 60_000 * reps)
+            e0.record()
+            for r in range(reps):
+                run(r)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / reps)
+        out[label] = (float(np.median(times)), 2 * n if not is_gemm else n)
+    del src, dst, scratch
+    return out
+
+
 def decode_study(step: Step, reps: int = 50):
     """Every small-M GEMM launch of a step (the 8B block decode, the 32B MLP
     tail at M=64, the 1.7B gate_up at M<=128) timed as in per_kernel_times,
@@ -968,6 +1019,12 @@ def main():
             hbm[label] = {"us": round(kt[label], 2), "gbs": round(gbs, 0),
                           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                           "frac_of_measured_ceiling": round(gbs / ref, 4)}
+    sizes = {label: (bool(flops), nbytes) for label, kind, flops, nbytes, _ in step.calls}
+    probes = size_matched_probes(step, [(label,) + sizes[label] for label in hbm])
+    for label, (pus, pbytes) in probes.items():
+        hbm[label]["size_matched_probe_us"] = round(pus, 2)
+        hbm[label]["size_matched_probe_gbs"] = round(pbytes / (pus * 1e-6) / 1e9, 0)
+        hbm[label]["probe_over_kernel_time"] = round(pus / kt[label], 4)
 
     # per-workload summary from the batched per-kernel times
     summary = {}
