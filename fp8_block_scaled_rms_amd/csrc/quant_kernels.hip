@@ -198,7 +198,10 @@ __device__ __forceinline__ void process_unit(const UnitPos& p, const uint4 (&xv)
       } else if constexpr (OP == kRms) {
         yo[2 * j] = (bf16_lo(vv[j]) * bf16_lo(ww[j])) * inv;  // x * w exact in fp32
         yo[2 * j + 1] = (bf16_hi(vv[j]) * bf16_hi(ww[j])) * inv;
-      } else {  // kSilu: gate in xv, up in wv
+      } else if constexpr (kKeepY) {  // kSilu: gate in xv, up in wv
+        yo[2 * j] = silu_bf16_branchy(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(ww[j]);
+        yo[2 * j + 1] = silu_bf16_branchy(vv[j] >> 16, silu_tab) * bf16_hi(ww[j]);
+      } else {
         yo[2 * j] = silu_bf16(vv[j] & 0xFFFFu, silu_tab) * bf16_lo(ww[j]);
         yo[2 * j + 1] = silu_bf16(vv[j] >> 16, silu_tab) * bf16_hi(ww[j]);
       }
