@@ -68,3 +68,18 @@ def test_quant_launch_config_matches_the_call_checks():
     tpr, ch, grid = fq.fp8q_quant_launch_config(fq.FRONT_RMSNORM, fq.GROUP128, 8192, 5120,
                                                 NUM_CUS)
     assert tpr in (64, 128, 256) and ch * 8 * tpr >= 5120 and grid > 0
+
+
+def test_rmsnorm_launches_loop_over_rows():
+    """RMSNorm launches are sized so that workgroups loop over rows (each
+    wave prefetches its next row): at the bench's large row counts a
+    workgroup handles more than one unit, so the GPU cases at those sizes run
+    the prefetching loop, including a prefetch past the last row."""
+    for M, K in [(2048, 5120), (8192, 5120), (2048, 2048)]:
+        tpr, ch, grid = fq.fp8q_quant_launch_config(fq.FRONT_RMSNORM, fq.GROUP128, M, K, NUM_CUS)
+        units_per_block = 256 // tpr
+        assert grid <= NUM_CUS * 3, (M, K, grid)  # at most 12 waves per compute unit
+        assert grid * units_per_block < M, (M, K, tpr, grid)
+    # the other front ends keep their larger grids
+    _, _, grid = fq.fp8q_quant_launch_config(fq.FRONT_IDENT, fq.GROUP128, 8192, 8192, NUM_CUS)
+    assert grid > NUM_CUS * 3
