@@ -700,47 +700,111 @@ def cpu_baseline(step: Step, label: str, rows: int):
                       f"N={N}, K={K}: {what}, {dt:.1f} s"}
 
 
+STACK = 8  # layers in the decode-stack graphs
+
+
+def _chain_times(torch, fn, per, reps):
+    """(GPU time per layer back to back, wall-clock latency per layer of one
+    call from an idle GPU) of fn, which issues `per` layers' chains."""
+    for _ in range(3):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    # longer than the host takes to issue the chains (~4 ms for one layer's,
+    # ~75 ms for a stack's when issued eagerly)
+    queue_ahead(torch, 8_000_000 if per == 1 else 20_000_000 * per)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    back_to_back = e0.elapsed_time(e1) * 1e3 / (reps * per)
+    lat = []
+    for _ in range(20):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        lat.append(time.perf_counter() - t0)
+    return round(back_to_back, 2), round(float(np.median(lat)) * 1e6 / per, 1)
+
+
+def _stack(step: Step, workload, M, stack_wts, rw):
+    from fp8_block_scaled_rms_amd.graph import LinearChain
+
+    mode, hidden, (qkv_n, o_k, gu_n, inter), _ = WORKLOADS[workload]
+    return [LinearChain(step.activations(M, hidden), step.activations(M, o_k),
+                        step.activations(M, hidden), rw, w, mode) for w in stack_wts]
+
+
+def _layer_weights(step: Step, workload):
+    mode, hidden, (qkv_n, o_k, gu_n, inter), _ = WORKLOADS[workload]
+    return {"qkv": step.weight(qkv_n, hidden, mode), "o_proj": step.weight(hidden, o_k, mode),
+            "gate_up": step.weight(gu_n, hidden, mode), "down": step.weight(hidden, inter, mode)}
+
+
 def decode_chain_latency(step: Step, Ms=(1, 8, 32), reps: int = 50):
     """The Qwen3-8B block-decode layer chain (8 launches) per M, launched
     eagerly through the C ABI and replayed from a HIP graph: the GPU time per
     chain back to back (between two events on the current stream, the chains
     queued behind a spin kernel so that the GPU never waits for the host), and
     the wall-clock latency of one chain from an idle GPU (issue, then
-    synchronize; median of 20)."""
-    from fp8_block_scaled_rms_amd.graph import LinearChain
+    synchronize; median of 20).  The same for a stack of STACK layers with
+    distinct weights (a decode step's linear work, its weights larger than
+    the last-level cache): eagerly, layer after layer, and as one graph
+    holding every layer's launches (capture_stack); those figures are per
+    layer.  The stack is also timed for the Qwen3-1.7B per-token layer, whose
+    kernels take less GPU time than the host needs to issue them."""
+    from fp8_block_scaled_rms_amd.graph import LinearChain, capture_stack
 
     torch = step.torch
-    mode, hidden, (qkv_n, o_k, gu_n, inter), _ = WORKLOADS["qwen3-8b-block-decode"]
-    wts = {"qkv": step.weight(qkv_n, hidden, mode), "o_proj": step.weight(hidden, o_k, mode),
-           "gate_up": step.weight(gu_n, hidden, mode), "down": step.weight(hidden, inter, mode)}
+    workload = "qwen3-8b-block-decode"
+    mode, hidden, (qkv_n, o_k, gu_n, inter), _ = WORKLOADS[workload]
+    stack_wts = [_layer_weights(step, workload) for _ in range(STACK)]
     rw = (1.0 + step.randn((hidden,), 0.1)).to(torch.bfloat16)
-    out = {"workload": "qwen3-8b-block-decode", "launches_per_chain": 8}
+    out = {"workload": workload, "launches_per_chain": 8, "stack_layers": STACK}
     for M in Ms:
         chain = LinearChain(step.activations(M, hidden), step.activations(M, o_k),
-                            step.activations(M, hidden), rw, wts, mode)
+                            step.activations(M, hidden), rw, stack_wts[0], mode)
         chain.capture()
+        stack = _stack(step, workload, M, stack_wts, rw)
+        stack_graph = capture_stack(stack)
+
+        def stack_eager():
+            for c in stack:
+                c.run()
+
         res = {}
-        for kind, fn in (("eager_us", chain.run), ("graph_us", chain.replay)):
-            for _ in range(3):
-                fn()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            queue_ahead(torch, 8_000_000)  # ~4 ms: longer than issuing the chains
-            e0.record()
-            for _ in range(reps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            res[kind] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
-            lat = []
-            for _ in range(20):
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                fn()
-                torch.cuda.synchronize()
-                lat.append(time.perf_counter() - t0)
-            res[kind.replace("_us", "_single_us")] = round(float(np.median(lat)) * 1e6, 1)
+        for kind, fn, per in (("eager", chain.run, 1), ("graph", chain.replay, 1),
+                              ("stack_eager", stack_eager, STACK),
+                              ("stack_graph", stack_graph.replay, STACK)):
+            sfx = "_per_layer" if per > 1 else ""
+            res[f"{kind}_us{sfx}"], res[f"{kind}_single_us{sfx}"] = _chain_times(
+                torch, fn, per, reps)
         out[f"M{M}"] = res
+        del stack, stack_graph, chain
+    del stack_wts
+
+    workload = "qwen3-1.7b-per-token"
+    mode, hidden, _, _ = WORKLOADS[workload]
+    small_wts = [_layer_weights(step, workload) for _ in range(STACK)]
+    rw = (1.0 + step.randn((hidden,), 0.1)).to(torch.bfloat16)
+    small = {"workload": workload, "stack_layers": STACK}
+    for M in (1, 16):
+        stack = _stack(step, workload, M, small_wts, rw)
+        stack_graph = capture_stack(stack)
+
+        def stack_eager():
+            for c in stack:
+                c.run()
+
+        res = {}
+        for kind, fn in (("stack_eager", stack_eager), ("stack_graph", stack_graph.replay)):
+            res[f"{kind}_us_per_layer"], res[f"{kind}_single_us_per_layer"] = _chain_times(
+                torch, fn, STACK, reps)
+        small[f"M{M}"] = res
+        del stack, stack_graph
+    out["stack_" + workload] = small
     return out
 
 

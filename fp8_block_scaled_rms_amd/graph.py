@@ -20,7 +20,8 @@ seven launches on the current stream through the C ABI (ctypes calls bound
 in advance); capture() records the same launches into a torch.cuda.CUDAGraph,
 whose replay then costs one launch.  None of the chain's launches records a
 memset or allocates, so a replay reads the inputs in place and rewrites
-every output.
+every output.  capture_stack() records the chains of several layers, each
+with its own weights, into one graph.
 """
 from __future__ import annotations
 
@@ -141,3 +142,27 @@ class LinearChain:
 
     def replay(self) -> None:
         self.graph.replay()
+
+
+def capture_stack(chains) -> torch.cuda.CUDAGraph:
+    """Record the chains of several decoder layers back to back into one
+    graph, as a decode step of a whole stack runs them (each chain with its
+    own weights and buffers).  One replay then issues every layer's launches
+    with a single host call, and the GPU runs them without the gap that
+    separates two replays."""
+    chains = list(chains)
+    if not chains:
+        raise ValueError("capture_stack needs at least one chain")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in chains:
+            c.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in chains:
+            c.run()
+    torch.cuda.synchronize()
+    return g

@@ -159,3 +159,37 @@ def test_chain_graph_at_qwen3_8b_decode_shape():
         assert _same(_snapshot(chain), eager), f"replay {rep}"
         chain.run()
         torch.cuda.synchronize()
+
+
+def test_stack_of_layers_in_one_graph_matches_eager():
+    """Three layers with distinct weights and inputs recorded into one graph
+    (capture_stack): every replay reproduces every layer's eager outputs,
+    with eager work between the replays."""
+    from fp8_block_scaled_rms_amd.graph import capture_stack
+
+    say("graph stack of 3 layers")
+    chains = []
+    for layer in range(3):
+        chain, host_in = _build(f"stack{layer}", 8, 512, 768, 512, 2048, 1024, fq.GROUP128)
+        chain.run()
+        torch.cuda.synchronize()
+        _check_eager_against_oracle(chain, host_in, fq.GROUP128)
+        chains.append(chain)
+    eager = [_snapshot(c) for c in chains]
+    assert not _same(eager[0], eager[1])
+    g = capture_stack(chains)
+    for rep in range(3):
+        for c in chains:
+            for t in c.outputs().values():
+                t.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for layer, c in enumerate(chains):
+            assert _same(_snapshot(c), eager[layer]), f"replay {rep}, layer {layer}"
+        for c in chains:
+            c.run()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for layer, c in enumerate(chains):
+            assert _same(_snapshot(c), eager[layer])
