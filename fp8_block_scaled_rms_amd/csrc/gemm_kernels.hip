@@ -479,10 +479,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
     for (int t = 0; t < S::kFT; ++t) acc[i][t] = acc_zero<E>();
 
-  // the fused kernel (SQ) keeps the previous block's token scales and its
-  // two weight scales (scalar registers) instead of their eight products:
-  // four VGPRs it needs to stay within 256
-  constexpr bool kScalarScales = kGroups && SQ;
+  // The fused kernel (SQ) scales each block's products at the end of that
+  // block (after its second half) rather than in the next block's first
+  // half, which also waits for that block's LDS fragments.  The plain
+  // kernels keep the FMAs in the first half, where their schedule measured
+  // faster.
+  constexpr bool kEndFma = kGroups && SQ;
 
   // the grouped loop issues the same number of loads per block throughout:
   // past the last block it loads the last block again, into its own buffer
@@ -618,9 +620,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 
   // The four substeps of one block on the rotated schedule; after_s1()
   // runs between substeps 1 and 2.  sprev(i, t): the previous block's
-  // scale product for weight fragment i and token fragment t.
+  // scale product for weight fragment i and token fragment t, applied in
+  // substep 0.  With END, the block's own products are instead scaled into
+  // the accumulators after its last substep, with scur(i, t) (the same
+  // products added in the same order, so the same sums).
   auto rotated_block = [&](v4f(&p)[S::kFW][S::kFT], auto sprev, const v8i(&xr)[S::kFT],
-                           const v8i(&wr)[S::kFW], auto after_s1) {
+                           const v8i(&wr)[S::kFW], auto after_s1, auto end_c, auto scur) {
+    constexpr bool END = decltype(end_c)::value;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v8h xh[S::kFT];
@@ -632,9 +638,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
 #pragma unroll
         for (int t = 0; t < S::kFT; ++t) {
           if (s == 0) {  // block j-1's products (zeros before the first block)
-            const float sp = sprev(i, t);
+            if constexpr (!END) {
+              const float sp = sprev(i, t);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
+              for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
+            }
             p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], v4f{0, 0, 0, 0}, 0, 0, 0);
           } else {
             p[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, xh[t], p[i][t], 0, 0, 0);
@@ -642,6 +650,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         }
       }
       if (s == 1) after_s1();
+    }
+    if constexpr (END) {
+#pragma unroll
+      for (int i = 0; i < S::kFW; ++i)
+#pragma unroll
+        for (int t = 0; t < S::kFT; ++t) {
+          const float sc = scur(i, t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sc, acc[i][t][r]);
+        }
     }
   };
 
@@ -657,21 +675,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     if constexpr (kGroups) {
       constexpr int L = S::kLoadsPerStage;
       const bool late = wave >= S::kWaves / 2;
-      // kScalarScales: the previous block's token scales, and its weight
-      // scales (the same for every lane of the wave: kept in scalar
-      // registers); their product is formed where it is applied.  Else
-      // sprev/sprev_hi hold the products.
-      float sarp[S::kFT], swp = 0.0f, swp_hi = 0.0f;
-#pragma unroll
-      for (int t = 0; t < S::kFT; ++t) sarp[t] = 0.0f;
-      auto uniform = [](float v) {
-        return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
-      };
+      // sprev/sprev_hi: the previous block's scale products (unused with
+      // kEndFma)
       auto scale_of = [&](int i, int t) {
-        if constexpr (kScalarScales)
-          return sarp[t] * ((SQ && i >= S::kFW / 2) ? swp_hi : swp);
-        else
-          return (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
+        return (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
       };
       // before the mid-block barrier this wave's LDS reads of block j have
       // returned (its buffer is refilled after the next barrier) and its
@@ -702,13 +709,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         read_block(j, xr, wr, sar, swr, swr_hi);
         load_block(j + ST - 1);
         prefetch_table(j);
-        rotated_block(p, scale_of, xr, wr, mid_barrier);
-        if constexpr (kScalarScales) {
-#pragma unroll
-          for (int t = 0; t < S::kFT; ++t) sarp[t] = sar[t];
-          swp = uniform(swr);
-          swp_hi = uniform(swr_hi);
-        } else {
+        rotated_block(p, scale_of, xr, wr, mid_barrier, std::integral_constant<bool, kEndFma>{},
+                      [&](int i, int t) {
+                        return sar[t] * ((SQ && i >= S::kFW / 2) ? swr_hi : swr);
+                      });
+        if constexpr (!kEndFma) {
 #pragma unroll
           for (int t = 0; t < S::kFT; ++t) {
             sprev[t] = sar[t] * swr;
@@ -718,13 +723,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
       }
       if (!late) __builtin_amdgcn_s_barrier();
       wait_vm<0>();  // the repeated loads of the last block
-      if constexpr (kScalarScales) {
-#pragma unroll
-        for (int t = 0; t < S::kFT; ++t) {
-          sprev[t] = sarp[t] * swp;
-          sprev_hi[t] = sarp[t] * swp_hi;
-        }
-      }
     } else {
       v8i xr[S::kFT], wr[S::kFW];
       float sar[S::kFT], swr = 0.0f, swr_hi = 0.0f;
@@ -739,7 +737,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
         rotated_block(
             p, [&](int i, int t) { return (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t]; },
-            xr, wr, []() {});
+            xr, wr, []() {}, std::false_type{}, [](int, int) { return 0.0f; });
 #pragma unroll
         for (int t = 0; t < S::kFT; ++t) {
           sprev[t] = sar[t] * swr;
@@ -748,14 +746,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
       }
     }
+    if constexpr (!kEndFma) {  // the last block's products
 #pragma unroll
-    for (int i = 0; i < S::kFW; ++i)
+      for (int i = 0; i < S::kFW; ++i)
 #pragma unroll
-      for (int t = 0; t < S::kFT; ++t) {
-        const float sp = (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
+        for (int t = 0; t < S::kFT; ++t) {
+          const float sp = (SQ && i >= S::kFW / 2) ? sprev_hi[t] : sprev[t];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
-      }
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sp, acc[i][t][r]);
+        }
+    }
   };
 
   auto k_loop = [&](auto fold_c) {
