@@ -16,9 +16,16 @@ namespace fp8q {
 //                 waves loads `split` (= j) K blocks at once; the waves are
 //                 reduced through LDS, and K longer than wk*j blocks is split
 //                 across workgroups through an fp32 workspace.
-// Both keep the weight rows on the 16-row side of the 16x16x128 MFMA and the
+//   kind kHybrid: two launches of tiled variants over column ranges of one
+//                 output: the weight-row tiles that fill whole rounds of
+//                 resident workgroups with variant part_a (bm x bn tiles, no
+//                 split), the remaining columns with variant part_b (split
+//                 along K), so the last round of part_a's tiles is not left
+//                 part-empty.  bm/bn/wm/wn describe part_a; split is
+//                 part_b's split-K factor.
+// All keep the weight rows on the 16-row side of the 16x16x128 MFMA and the
 // tokens on the 16-column side (the swap-AB orientation).
-enum GemmKind { kTiled = 0, kSkinny = 1 };
+enum GemmKind { kTiled = 0, kSkinny = 1, kHybrid = 2 };
 
 // Accumulation engine (see gemm_kernels.hip): 0 = FP8 MFMA (fast, hardware
 // group-truncated sums), 1 = exact f16 MFMA on losslessly widened operands,
@@ -33,6 +40,7 @@ struct GemmConfig {
   int bm, bn, wm, wn;  // kTiled
   int tm, rw, wk;      // kSkinny
   int split;           // kSkinny: K blocks per wave (j); kTiled: split-K factor
+  int part_a, part_b;  // kHybrid: the two tiled variants (registry ids)
 };
 
 int gemm_num_configs();

@@ -40,6 +40,7 @@
 #include "silu_table.hpp"
 #include "gemm_kernels.h"
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <memory>
@@ -297,12 +298,15 @@ __device__ __forceinline__ void wait_stage(int after) {
 // rows are 32 gate rows and the 32 matching up rows, so a lane holds the
 // gate and up values of the same output columns, and the 128 output columns
 // of a workgroup are one quantization group.
+// The bf16 output's rows are ldy elements apart (N, or the whole width when
+// a launch covers a column range of a wider output); split-K partials and
+// the fused epilogue's codes are laid out by N.
 template <int BM, int BN, int WM, int WN, int ST, bool BLOCK, int E, int PRIO = 0,
           bool P2 = false, bool SQ = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
     uint16_t* __restrict__ y, float* __restrict__ ws, const uint8_t* __restrict__ A,
     const float* __restrict__ sa, const uint8_t* __restrict__ B, const float* __restrict__ sb,
-    int M, int N, int K, int SPLIT) {
+    int M, int N, int K, int SPLIT, int ldy) {
   using S = TiledShape<BM, BN, WM, WN, ST, BLOCK>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -928,13 +932,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled_kernel(
         v[2] = v[2] * sm * s4.z;
         v[3] = v[3] * sm * s4.w;
       }
-      store_bf16x4(y + static_cast<long>(m) * N + n, v[0], v[1], v[2], v[3]);
+      store_bf16x4(y + static_cast<long>(m) * ldy + n, v[0], v[1], v[2], v[3]);
     }
   }
 }
 
 // ------------------------------------------------------------ skinny --
-// Small M: the weight matrix is the HBM traffic, so the kernel is built to
+// Small M (output rows ldy elements apart, as in the tiled kernel): the
+// weight matrix is the HBM traffic, so the kernel is built to
 // keep enough bytes in flight.  A workgroup owns RW*16 weight rows and all
 // tokens (<= TMX*16); each of its WK waves owns J K blocks (interleaved
 // across the waves) and issues the loads of all of them before the first
@@ -945,7 +950,7 @@ template <int TMX, int RW, int WK, int J, bool BLOCK, int E>
 __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
     uint16_t* __restrict__ y, float* __restrict__ ws, const uint8_t* __restrict__ A,
     const float* __restrict__ sa, const uint8_t* __restrict__ B, const float* __restrict__ sb,
-    int M, int N, int K, int SPLIT) {
+    int M, int N, int K, int SPLIT, int ldy) {
   extern __shared__ __attribute__((aligned(16))) float red[];  // [WK][RW*TMX][64] v4f
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1078,7 +1083,7 @@ __global__ __launch_bounds__(WK * 64) void gemm_skinny_kernel(
       v[2] = v[2] * sm * s4.z;
       v[3] = v[3] * sm * s4.w;
     }
-    store_bf16x4(y + static_cast<long>(m) * N + n, v[0], v[1], v[2], v[3]);
+    store_bf16x4(y + static_cast<long>(m) * ldy + n, v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -1094,7 +1099,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict
                                                             const float* __restrict__ ws,
                                                             const float* __restrict__ sa,
                                                             const float* __restrict__ sb,
-                                                            int M, int N, int SPLIT) {
+                                                            int M, int N, int SPLIT,
+                                                            int ldy) {
   typedef typename std::conditional<INT, int4, float4>::type V;
   const long total = static_cast<long>(M) * (N / 4);
   const long plane = static_cast<long>(M) * N;  // floats per split
@@ -1131,7 +1137,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(uint16_t* __restrict
       v.z = v.z * sm * s4.z;
       v.w = v.w * sm * s4.w;
     }
-    store_bf16x4(y + static_cast<long>(m) * N + n, v.x, v.y, v.z, v.w);
+    store_bf16x4(y + static_cast<long>(m) * ldy + n, v.x, v.y, v.z, v.w);
   }
 }
 
@@ -1208,6 +1214,25 @@ Variant skinny_variant() {
   return v;
 }
 
+// A kHybrid variant of two registered tiled variants: `a` unsplit over the
+// columns that fill whole rounds of workgroups, `b` (split along K) over the
+// rest.  Named after `a` with suffix _h<b's split>.
+Variant hybrid_variant(const std::vector<Variant>& v, const char* a, const char* b) {
+  int ia = -1, ib = -1;
+  for (size_t i = 0; i < v.size(); ++i) {
+    if (std::strcmp(v[i].cfg.name, a) == 0) ia = static_cast<int>(i);
+    if (std::strcmp(v[i].cfg.name, b) == 0) ib = static_cast<int>(i);
+  }
+  Variant h{};
+  if (ia < 0 || ib < 0) std::abort();  // a registry-construction bug, not a user error
+  const GemmConfig& ca = v[ia].cfg;
+  const GemmConfig& cb = v[ib].cfg;
+  const char* name = keep_name(std::string(ca.name) + "_h" + std::to_string(cb.split));
+  h.cfg = GemmConfig{name, kHybrid, ca.engine, ca.bm, ca.bn, ca.wm, ca.wn, 0, 0, 0, cb.split,
+                     ia, ib};
+  return h;
+}
+
 // FP8Q_NONCONFORMING_FP8_MFMA=1: also register the FP8-MFMA engine's variants.
 bool nonconforming_fp8_requested() {
   const char* v = std::getenv("FP8Q_NONCONFORMING_FP8_MFMA");
@@ -1238,6 +1263,10 @@ std::vector<Variant>& registry() {
     v.push_back(tiled_variant<64, 128, 1, 2, 3, kEngineF16, 0, 16>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 0, 2>());
     v.push_back(tiled_variant<128, 128, 2, 2, 2, kEngineF16, 0, 4>());
+    // whole rounds of unsplit 128x256 tiles, the remaining columns split 2 or
+    // 4 ways on 128x128 tiles
+    v.push_back(hybrid_variant(v, "f16_tiled_m128_n256_w2x4_st3", "f16_tiled_m128_n128_w2x2_st2_s2"));
+    v.push_back(hybrid_variant(v, "f16_tiled_m128_n256_w2x4_st3", "f16_tiled_m128_n128_w2x2_st2_s4"));
     // the FP8-MFMA engine misses the accuracy contract (group truncation, see
     // kEngineF8): registered only on explicit request, for measurements
     if (nonconforming_fp8_requested()) {
@@ -1363,6 +1392,7 @@ const GemmConfig& gemm_config(int id) { return registry()[id].cfg; }
 bool gemm_config_fits(int id, long M, long N, long K) {
   const GemmConfig& c = gemm_config(id);
   if (c.kind == kTiled) return N % c.bn == 0;
+  if (c.kind == kHybrid) return N % gemm_config(c.part_b).bn == 0;
   if (M > 16L * c.tm) return false;
   if (N % (16L * c.rw)) return false;
   return true;
@@ -1388,16 +1418,68 @@ int split_of(const GemmConfig& c, long K) {
   return c.kind == kSkinny ? skinny_split(c, K) : tiled_split(c, K);
 }
 
+// Compute units of the current device, cached per device; 256 (an MI355X)
+// where no device answers (a workspace-size query on a host without a GPU).
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      c <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cus[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+// Column split of a kHybrid launch: part_a takes na columns, whole bn-wide
+// tiles of every token-tile row that together fill whole rounds of resident
+// workgroups; part_b the nt remaining columns (a multiple of its tile width,
+// as N is).  na = 0 when the tiles do not fill one round; nt = 0 when they
+// fill whole rounds exactly.
+struct ColumnSplit {
+  int na, nt;
+};
+ColumnSplit hybrid_columns(const GemmConfig& c, long M, long N) {
+  const Variant& va = registry()[c.part_a];
+  // part_a's workgroups per CU: bounded by its LDS ring (160 KiB per CU) and
+  // by two waves per SIMD (eight per CU)
+  long per_cu = (160L * 1024) / static_cast<long>(va.lds);
+  const long by_waves = 8L * 64 / va.threads;
+  if (by_waves < per_cu) per_cu = by_waves;
+  if (per_cu < 1) per_cu = 1;
+  const long slots = per_cu * device_cus();
+  const long rows = (M + c.bm - 1) / c.bm, cols = N / c.bn;
+  const long whole = (rows * cols / slots) * slots;
+  long na_cols = whole / rows;
+  if (na_cols > cols) na_cols = cols;
+  const long na = na_cols * c.bn;
+  return {static_cast<int>(na), static_cast<int>(N - na)};
+}
+
 size_t gemm_workspace_bytes(int id, long M, long N, long K) {
-  const int split = split_of(gemm_config(id), K);
+  const GemmConfig& c = gemm_config(id);
+  if (c.kind == kHybrid) {
+    const ColumnSplit cs = hybrid_columns(c, M, N);
+    return cs.nt > 0 ? gemm_workspace_bytes(c.part_b, M, cs.nt, K) : 0;
+  }
+  const int split = split_of(c, K);
   if (split <= 1) return 0;
   return static_cast<size_t>(split) * M * N * sizeof(float);
 }
 
-hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const float* sa,
-                       const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
-                       hipStream_t st) {
-  const Variant& v = registry()[id];
+// One launch of a tiled or skinny variant over N output columns whose rows
+// lie ldy elements apart in y (then the split-K reduction, if any).
+hipError_t launch_one(const Variant& v, int scales, uint16_t* y, const uint8_t* a,
+                      const float* sa, const uint8_t* b, const float* sb, int M, int N, int K,
+                      int ldy, void* ws, hipStream_t st) {
   const int bw = scales;
   const bool blockwise = scales != kScalesPerToken;
   if (v.fn[bw] == nullptr) return hipErrorInvalidDeviceFunction;
@@ -1405,7 +1487,7 @@ hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const 
   int split = split_of(v.cfg, K);
   float* wsf = static_cast<float*>(ws);
   {
-    void* args[] = {&y, &wsf, &a, &sa, &b, &sb, &M, &N, &K, &split};
+    void* args[] = {&y, &wsf, &a, &sa, &b, &sb, &M, &N, &K, &split, &ldy};
     const dim3 grid = v.cfg.kind == kTiled
                           ? dim3((N / v.cfg.bn) * ((M + v.cfg.bm - 1) / v.cfg.bm), split)
                           : dim3(N / (16 * v.cfg.rw), split);
@@ -1418,14 +1500,33 @@ hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const 
   if (blocks > 8192) blocks = 8192;
   if (blockwise)
     hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), dim3(blocks), dim3(256), 0, st, y,
-                       wsf, sa, sb, M, N, split);
+                       wsf, sa, sb, M, N, split, ldy);
   else if (v.cfg.engine == kEngineI8)
     hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), dim3(blocks), dim3(256), 0, st, y,
-                       wsf, sa, sb, M, N, split);
+                       wsf, sa, sb, M, N, split, ldy);
   else
     hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), dim3(blocks), dim3(256), 0, st, y,
-                       wsf, sa, sb, M, N, split);
+                       wsf, sa, sb, M, N, split, ldy);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const float* sa,
+                       const uint8_t* b, const float* sb, int M, int N, int K, void* ws,
+                       hipStream_t st) {
+  const Variant& v = registry()[id];
+  if (v.cfg.kind != kHybrid) return launch_one(v, scales, y, a, sa, b, sb, M, N, K, N, ws, st);
+  // part_a on columns [0, na), part_b on [na, N): the weight rows, their
+  // scales and the output columns of each range, rows of y N apart
+  const ColumnSplit cs = hybrid_columns(v.cfg, M, N);
+  if (cs.na > 0) {
+    const hipError_t e =
+        launch_one(registry()[v.cfg.part_a], scales, y, a, sa, b, sb, M, cs.na, K, N, nullptr, st);
+    if (e != hipSuccess || cs.nt == 0) return e;
+  }
+  const long kb = K / kBK;
+  const float* sb_t = scales == kScalesPerToken ? sb + cs.na : sb + (cs.na / 128) * kb;
+  return launch_one(registry()[v.cfg.part_b], scales, y + cs.na, a, sa,
+                    b + static_cast<long>(cs.na) * K, sb_t, M, cs.nt, K, N, ws, st);
 }
 
 hipError_t launch_gemm_silu_quant(uint8_t* q, float* scale, const uint8_t* a, const float* sa,
@@ -1437,8 +1538,8 @@ hipError_t launch_gemm_silu_quant(uint8_t* q, float* scale, const uint8_t* a, co
   const size_t lds = TiledShape<kBM, kBN, kWM, kWN, kST, true>::kLds;
   ensure_fn_lds(fn, lds);
   uint16_t* y = reinterpret_cast<uint16_t*>(q);
-  int split = 1;
-  void* args[] = {&y, &scale, &a, &sa, &b, &sb, &M, &N, &K, &split};
+  int split = 1, ldy = N;  // (the fused epilogue writes q and scale by D)
+  void* args[] = {&y, &scale, &a, &sa, &b, &sb, &M, &N, &K, &split, &ldy};
   const dim3 grid((N / kBN) * ((M + kBM - 1) / kBM), 1);
   return hipLaunchKernel(fn, grid, dim3(kWM * kWN * 64), args, lds, st);
 }

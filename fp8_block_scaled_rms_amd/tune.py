@@ -8,7 +8,8 @@ aihirek.info, section "Autotuning picks the right variant": the algorithm is
 a tuned parameter chosen per shape instead of a hand-written rule).
 
     python -m fp8_block_scaled_rms_amd.tune --out results.jsonl [--write-table PATH]
-        [--engine exact|fp8|all] [--shapes default|quick]
+        [--engine exact|fp8|all] [--shapes default|quick|large|int8|small|tail]
+        [--remeasure]
     python -m fp8_block_scaled_rms_amd.tune --from-results RESULTS --write-table PATH
 
 Results are appended to a JSONL file, one line per (shape, variant), and a
@@ -58,6 +59,10 @@ QUICK = [(BW, 8192, 51200, 5120), (BW, 2048, 10240, 5120), (BW, 32, 24576, 4096)
          (BW, 1, 4096, 4096), (MM, 2048, 12288, 2048), (MM, 128, 12288, 2048)]
 LARGE = [(BW, M, N, K) for M in (2048, 8192)
          for N, K in ((10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600))]
+# shapes whose 128x256 tiles leave the last round of workgroups part-empty
+# (where the hybrid variants can differ from their unsplit part)
+TAIL = [(BW, 2048, 10240, 5120), (BW, 2048, 5120, 8192), (BW, 2048, 5120, 25600),
+        (BW, 4096, 5120, 25600)]
 
 
 def variants(op, M, N, K, engine):
@@ -212,7 +217,10 @@ def main():
     ap.add_argument("--out", default="tune_results.jsonl")
     ap.add_argument("--engine", default="exact", choices=["exact", "fp8", "all"])
     ap.add_argument("--shapes", default="default",
-                    choices=["default", "quick", "large", "int8", "small"])
+                    choices=["default", "quick", "large", "int8", "small", "tail"])
+    ap.add_argument("--remeasure", action="store_true",
+                    help="first drop the results file's rows of the selected shapes, so that "
+                         "every variant of each is timed again in this run")
     ap.add_argument("--write-table", default=None, help="path of the table to write")
     ap.add_argument("--from-results", default=None,
                     help="write the table from this results file without measuring")
@@ -223,10 +231,19 @@ def main():
             ap.error("--from-results needs --write-table")
         write_table(exact_choices(load_results(args.from_results)), args.write_table)
         return
-    done = load_results(args.out)
-    shapes = {"default": SHAPES, "quick": QUICK, "large": LARGE,
+    shapes = {"default": SHAPES, "quick": QUICK, "large": LARGE, "tail": TAIL,
               "int8": [sh for sh in SHAPES if sh[0] == I8],
               "small": [sh for sh in SHAPES if sh[0] != I8 and sh[1] <= 128]}[args.shapes]
+    if args.remeasure and os.path.exists(args.out):
+        keep = []
+        with open(args.out) as f:
+            for line in f:
+                r = json.loads(line) if line.strip() else None
+                if r is not None and (r["op"], r["M"], r["N"], r["K"]) not in shapes:
+                    keep.append(line if line.endswith("\n") else line + "\n")
+        with open(args.out, "w") as f:
+            f.writelines(keep)
+    done = load_results(args.out)
     with open(args.out, "a") as f:
         for op, M, N, K in shapes:
             cands = variants(op, M, N, K, args.engine)

@@ -222,8 +222,8 @@ int fp8q_scaled_mm_blockwise_ue8m0(void* y, const void* a, const void* b, const 
  * Returns FP8Q_ERR_WORKSPACE, before touching the device, when the shape's
  * variant needs more than FP8Q_NOALLOC_SCRATCH_BYTES of partials, i.e. when
  * fp8q_workspace_size(FP8Q_OP_SCALED_MM_BLOCKWISE, M, N, K) exceeds it (the
- * decode and small-M shapes need at most 20 MiB; long-K shapes at large M
- * can need more).
+ * Qwen3 shapes need at most 32 MiB; a long K split across all columns of a
+ * mid-size M can need more, e.g. 80 MiB at M=1024, N=5120, K=25600).
  * All calls on one GPU share its scratch array: calls whose executions
  * overlap on one GPU (concurrent streams, or threads) race on it and give
  * undefined results.  Calls ordered on one stream are safe.

@@ -144,13 +144,16 @@ def test_noalloc_gemm_argument_checks():
     assert f(A + 2, B, C, D, E, 4, 256, 256, None) == ALIGN
     # a shape whose table variant needs more split-K partials than the
     # scratch array holds is refused on the host, before any device call
-    M, N, K = 2048, 5120, 25600
+    # (M=1024 x N=5120 x K=25600: every column split four ways, 84 MB)
+    M, N, K = 1024, 5120, 25600
     assert fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, M, N, K) > 64 << 20
     assert f(A, B, C, D, E, M, N, K, None) == WS
-    # every decode / small-M blockwise shape of the workloads fits
+    # every blockwise shape of the workloads fits
     decode = [(M, N, K) for M in (1, 2, 4, 8, 16, 32)
               for N, K in ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288))]
-    for M, N, K in decode + [(64, 5120, 25600)]:
+    prefill = [(M, N, K) for M in (2048, 8192)
+               for N, K in ((10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600))]
+    for M, N, K in decode + prefill + [(64, 5120, 25600), (4096, 5120, 25600)]:
         assert fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, M, N, K) <= 64 << 20
 
 

@@ -248,6 +248,60 @@ def test_gemm_writes_stay_in_bounds(cfg, name):
     assert torch.all(wsbuf[:64] == -1.0) and torch.all(wsbuf[64 + nws // 4:] == -1.0)
 
 
+HYBRIDS = ["f16_tiled_m128_n256_w2x4_st3_h2", "f16_tiled_m128_n256_w2x4_st3_h4"]
+
+
+@pytest.mark.parametrize("name", HYBRIDS)
+@pytest.mark.parametrize("op", [MM, BW], ids=["mm", "blockwise"])
+def test_hybrid_columns_equal_their_two_variants(op, name):
+    """A hybrid variant at a shape with more 128x256 tiles than one round of
+    workgroups (16 token-tile rows x 20 column tiles, one workgroup per CU):
+    the columns that fill whole rounds equal, bit for bit, the unsplit
+    128x256 variant's output, and the rest the split 128x128 variant's, each
+    run alone on the whole problem; nothing outside y or the workspace is
+    written, and sampled rows meet the acceptance rule."""
+    M, N, K = 2048, 5120, 1024
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows, cols = M // 128, N // 256
+    na = (rows * cols // cus) * cus // rows * 256
+    assert 0 < na < N
+    names = {fq.fp8q_gemm_config_name(i): i for i in range(fq.fp8q_gemm_num_configs())}
+    part_b = "f16_tiled_m128_n128_w2x2_st2_s" + name[-1]
+    say("gemm hybrid", name, op, M, N, K, "columns", na)
+    rng = synth.rng_for("hybrid", name, op, M, N, K)
+    a_h = synth.gen_e4m3_codes(rng, (M, K))
+    b_h = synth.gen_e4m3_codes(rng, (N, K))
+    sa_h, sb_h = _scales(rng, op, M, N, K)
+    a, b, sa, sb = u8_dev(a_h), u8_dev(b_h), f32_dev(sa_h), f32_dev(sb_h)
+
+    def run(cfg, guard=False):
+        buf = torch.full((M * N + 1024,), 3.0, dtype=torch.bfloat16, device=DEV)
+        y = buf[512:512 + M * N].view(M, N)
+        nws = fq.fp8q_workspace_size(op, M, N, K, cfg)
+        wsbuf = torch.full(((nws // 4) + 128,), -1.0, dtype=torch.float32, device=DEV)
+        ws = wsbuf[64:64 + nws // 4] if nws else None
+        if op == MM:
+            fq.fp8q_scaled_mm(y, a, b, sa, sb, ws, cfg)
+        else:
+            fq.fp8q_scaled_mm_blockwise(y, a, b, sa, sb, ws, cfg)
+        torch.cuda.synchronize()
+        if guard:
+            assert torch.all(buf[:512] == 3.0) and torch.all(buf[512 + M * N:] == 3.0)
+            assert torch.all(wsbuf[:64] == -1.0) and torch.all(wsbuf[64 + nws // 4:] == -1.0)
+        return y
+
+    y_h = run(names[name], guard=True)
+    y_a = run(names["f16_tiled_m128_n256_w2x4_st3"])
+    y_b = run(names[part_b])
+    assert torch.equal(y_h[:, :na].view(torch.int16), y_a[:, :na].view(torch.int16))
+    assert torch.equal(y_h[:, na:].view(torch.int16), y_b[:, na:].view(torch.int16))
+    rows_s = synth.rng_for("hybrid-rows", name, op).choice(M, 48, replace=False)
+    rows_s.sort()
+    sa_rows = sa_h[rows_s]
+    res = gemm.acceptance(bf16_host_f64(y_h)[rows_s], _ref(op, a_h[rows_s], sa_rows, b_h, sb_h))
+    assert res["ok"], res
+
+
 def test_gemm_m_zero_is_noop():
     a = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
     b = torch.zeros((256, 256), dtype=torch.uint8, device=DEV)

@@ -36,13 +36,14 @@ def test_table_names_registered_exact_variants():
 def test_noalloc_test_shapes_split_k():
     """tests/test_zz_no_alloc.py exercises the scratch array on shapes whose
     table variant splits K; a regenerated table must keep them splitting."""
-    pairs = [((64, 5120, 25600), (32, 4096, 12288)), ((32, 4096, 12288), (16, 4096, 12288))]
+    pairs = [((4096, 5120, 25600), (64, 5120, 25600)), ((64, 5120, 25600), (32, 4096, 12288)),
+             ((32, 4096, 12288), (16, 4096, 12288))]
     for pair in pairs:
         needs = [fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, *s) for s in pair]
         assert all(n > 0 for n in needs), (pair, needs)
         assert needs[1] < needs[0], (pair, needs)  # the second call is the smaller
         assert needs[0] <= 64 << 20
-    big = fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, 2048, 5120, 25600)
+    big = fq.fp8q_workspace_size(fq.OP_SCALED_MM_BLOCKWISE, 1024, 5120, 25600)
     assert big > 64 << 20  # the oversized case the no-alloc entry rejects
 
 
