@@ -1224,7 +1224,11 @@ Variant hybrid_variant(const std::vector<Variant>& v, const char* a, const char*
     if (std::strcmp(v[i].cfg.name, b) == 0) ib = static_cast<int>(i);
   }
   Variant h{};
-  if (ia < 0 || ib < 0) std::abort();  // a registry-construction bug, not a user error
+  if (ia < 0 || ib < 0) {  // not registered: a variant that fits no shape
+    h.cfg = GemmConfig{keep_name(std::string(a) + "_h_unavailable"), kHybrid, kEngineF16,
+                       0, 0, 0, 0, 0, 0, 0, 0, -1, -1};
+    return h;
+  }
   const GemmConfig& ca = v[ia].cfg;
   const GemmConfig& cb = v[ib].cfg;
   const char* name = keep_name(std::string(ca.name) + "_h" + std::to_string(cb.split));
@@ -1392,7 +1396,7 @@ const GemmConfig& gemm_config(int id) { return registry()[id].cfg; }
 bool gemm_config_fits(int id, long M, long N, long K) {
   const GemmConfig& c = gemm_config(id);
   if (c.kind == kTiled) return N % c.bn == 0;
-  if (c.kind == kHybrid) return N % gemm_config(c.part_b).bn == 0;
+  if (c.kind == kHybrid) return c.part_b >= 0 && N % gemm_config(c.part_b).bn == 0;
   if (M > 16L * c.tm) return false;
   if (N % (16L * c.rw)) return false;
   return true;
@@ -1467,6 +1471,7 @@ ColumnSplit hybrid_columns(const GemmConfig& c, long M, long N) {
 size_t gemm_workspace_bytes(int id, long M, long N, long K) {
   const GemmConfig& c = gemm_config(id);
   if (c.kind == kHybrid) {
+    if (c.part_a < 0 || c.part_b < 0) return 0;
     const ColumnSplit cs = hybrid_columns(c, M, N);
     return cs.nt > 0 ? gemm_workspace_bytes(c.part_b, M, cs.nt, K) : 0;
   }
@@ -1515,6 +1520,7 @@ hipError_t launch_gemm(int id, int scales, uint16_t* y, const uint8_t* a, const 
                        hipStream_t st) {
   const Variant& v = registry()[id];
   if (v.cfg.kind != kHybrid) return launch_one(v, scales, y, a, sa, b, sb, M, N, K, N, ws, st);
+  if (v.cfg.part_a < 0 || v.cfg.part_b < 0) return hipErrorInvalidDeviceFunction;
   // part_a on columns [0, na), part_b on [na, N): the weight rows, their
   // scales and the output columns of each range, rows of y N apart
   const ColumnSplit cs = hybrid_columns(v.cfg, M, N);
