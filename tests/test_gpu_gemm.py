@@ -302,6 +302,38 @@ def test_hybrid_columns_equal_their_two_variants(op, name):
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("name", HYBRIDS)
+def test_hybrid_ue8m0_columns_equal_their_two_variants(name):
+    """The UE8M0 entry point on a hybrid variant, with power-of-two scales at
+    a shape where both parts run: the first part's eight-wave tiles fold the
+    scales into the widening, the second part's four-wave tiles take the
+    general path; each part's columns equal, bit for bit, that variant run
+    alone through the same entry point, and sampled rows meet the
+    acceptance rule."""
+    M, N, K = 2048, 5120, 1024
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    na = ((M // 128) * (N // 256) // cus) * cus // (M // 128) * 256
+    assert 0 < na < N
+    names = {fq.fp8q_gemm_config_name(i): i for i in range(fq.fp8q_gemm_num_configs())}
+    part_b = "f16_tiled_m128_n128_w2x2_st2_s" + name[-1]
+    say("gemm hybrid ue8m0", name, M, N, K, "columns", na)
+    rng = synth.rng_for("hybrid-ue8m0", name, M, N, K)
+    a_h = synth.gen_e4m3_codes(rng, (M, K))
+    b_h = synth.gen_e4m3_codes(rng, (N, K))
+    sa_h, sb_h = _scales(rng, BW, M, N, K, pow2=True)
+    a, b, sa, sb = u8_dev(a_h), u8_dev(b_h), f32_dev(sa_h), f32_dev(sb_h)
+    y_h = fq.scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg=names[name])
+    y_a = fq.scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg=names["f16_tiled_m128_n256_w2x4_st3"])
+    y_b = fq.scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg=names[part_b])
+    torch.cuda.synchronize()
+    assert torch.equal(y_h[:, :na].view(torch.int16), y_a[:, :na].view(torch.int16))
+    assert torch.equal(y_h[:, na:].view(torch.int16), y_b[:, na:].view(torch.int16))
+    rows_s = synth.rng_for("hybrid-ue8m0-rows", name).choice(M, 48, replace=False)
+    rows_s.sort()
+    res = gemm.acceptance(bf16_host_f64(y_h)[rows_s], _ref(BW, a_h[rows_s], sa_h[rows_s], b_h, sb_h))
+    assert res["ok"], res
+
+
 def test_gemm_m_zero_is_noop():
     a = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
     b = torch.zeros((256, 256), dtype=torch.uint8, device=DEV)
