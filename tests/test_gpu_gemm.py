@@ -251,22 +251,33 @@ def test_gemm_writes_stay_in_bounds(cfg, name):
 HYBRIDS = ["f16_tiled_m128_n256_w2x4_st3_h2", "f16_tiled_m128_n256_w2x4_st3_h4"]
 
 
+def _hybrid_parts(name, M, N):
+    """The hybrid's two variants and the columns its unsplit part takes: the
+    bn-wide column tiles of every token-tile row that fill whole rounds of
+    resident workgroups (one eight-wave 128x256 or two four-wave 128x128
+    workgroups per CU)."""
+    part_a, split = name.rsplit("_h", 1)
+    bn = int(part_a.split("_n")[1].split("_")[0])
+    per_cu = 1 if bn == 256 else 2
+    slots = per_cu * torch.cuda.get_device_properties(0).multi_processor_count
+    rows, cols = -(-M // 128), N // bn
+    na = (rows * cols // slots) * slots // rows * bn
+    return part_a, "f16_tiled_m128_n128_w2x2_st2_s" + split, min(na, cols * bn)
+
+
 @pytest.mark.parametrize("name", HYBRIDS)
 @pytest.mark.parametrize("op", [MM, BW], ids=["mm", "blockwise"])
 def test_hybrid_columns_equal_their_two_variants(op, name):
-    """A hybrid variant at a shape with more 128x256 tiles than one round of
-    workgroups (16 token-tile rows x 20 column tiles, one workgroup per CU):
-    the columns that fill whole rounds equal, bit for bit, the unsplit
-    128x256 variant's output, and the rest the split 128x128 variant's, each
-    run alone on the whole problem; nothing outside y or the workspace is
-    written, and sampled rows meet the acceptance rule."""
+    """A hybrid variant at a shape with more tiles than one round of
+    workgroups (M=2048, N=5120): the columns that fill whole rounds equal,
+    bit for bit, the unsplit variant's output, and the rest the split
+    128x128 variant's, each run alone on the whole problem; nothing outside
+    y or the workspace is written, and sampled rows meet the acceptance
+    rule."""
     M, N, K = 2048, 5120, 1024
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    rows, cols = M // 128, N // 256
-    na = (rows * cols // cus) * cus // rows * 256
+    part_a, part_b, na = _hybrid_parts(name, M, N)
     assert 0 < na < N
     names = {fq.fp8q_gemm_config_name(i): i for i in range(fq.fp8q_gemm_num_configs())}
-    part_b = "f16_tiled_m128_n128_w2x2_st2_s" + name[-1]
     say("gemm hybrid", name, op, M, N, K, "columns", na)
     rng = synth.rng_for("hybrid", name, op, M, N, K)
     a_h = synth.gen_e4m3_codes(rng, (M, K))
@@ -291,7 +302,7 @@ def test_hybrid_columns_equal_their_two_variants(op, name):
         return y
 
     y_h = run(names[name], guard=True)
-    y_a = run(names["f16_tiled_m128_n256_w2x4_st3"])
+    y_a = run(names[part_a])
     y_b = run(names[part_b])
     assert torch.equal(y_h[:, :na].view(torch.int16), y_a[:, :na].view(torch.int16))
     assert torch.equal(y_h[:, na:].view(torch.int16), y_b[:, na:].view(torch.int16))
@@ -305,17 +316,14 @@ def test_hybrid_columns_equal_their_two_variants(op, name):
 @pytest.mark.parametrize("name", HYBRIDS)
 def test_hybrid_ue8m0_columns_equal_their_two_variants(name):
     """The UE8M0 entry point on a hybrid variant, with power-of-two scales at
-    a shape where both parts run: the first part's eight-wave tiles fold the
-    scales into the widening, the second part's four-wave tiles take the
-    general path; each part's columns equal, bit for bit, that variant run
-    alone through the same entry point, and sampled rows meet the
-    acceptance rule."""
+    a shape where both parts run (eight-wave tiles fold the scales into the
+    widening, four-wave tiles take the general path): each part's columns
+    equal, bit for bit, that variant run alone through the same entry point,
+    and sampled rows meet the acceptance rule."""
     M, N, K = 2048, 5120, 1024
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    na = ((M // 128) * (N // 256) // cus) * cus // (M // 128) * 256
+    part_a, part_b, na = _hybrid_parts(name, M, N)
     assert 0 < na < N
     names = {fq.fp8q_gemm_config_name(i): i for i in range(fq.fp8q_gemm_num_configs())}
-    part_b = "f16_tiled_m128_n128_w2x2_st2_s" + name[-1]
     say("gemm hybrid ue8m0", name, M, N, K, "columns", na)
     rng = synth.rng_for("hybrid-ue8m0", name, M, N, K)
     a_h = synth.gen_e4m3_codes(rng, (M, K))
@@ -323,7 +331,7 @@ def test_hybrid_ue8m0_columns_equal_their_two_variants(name):
     sa_h, sb_h = _scales(rng, BW, M, N, K, pow2=True)
     a, b, sa, sb = u8_dev(a_h), u8_dev(b_h), f32_dev(sa_h), f32_dev(sb_h)
     y_h = fq.scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg=names[name])
-    y_a = fq.scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg=names["f16_tiled_m128_n256_w2x4_st3"])
+    y_a = fq.scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg=names[part_a])
     y_b = fq.scaled_mm_blockwise_ue8m0(a, b, sa, sb, cfg=names[part_b])
     torch.cuda.synchronize()
     assert torch.equal(y_h[:, :na].view(torch.int16), y_a[:, :na].view(torch.int16))
