@@ -265,16 +265,17 @@ def _hybrid_parts(name, M, N):
     return part_a, "f16_tiled_m128_n128_w2x2_st2_s" + split, min(na, cols * bn)
 
 
+@pytest.mark.parametrize("M", [2048, 1999])
 @pytest.mark.parametrize("name", HYBRIDS)
 @pytest.mark.parametrize("op", [MM, BW], ids=["mm", "blockwise"])
-def test_hybrid_columns_equal_their_two_variants(op, name):
+def test_hybrid_columns_equal_their_two_variants(op, name, M):
     """A hybrid variant at a shape with more tiles than one round of
-    workgroups (M=2048, N=5120): the columns that fill whole rounds equal,
+    workgroups (M=2048, and a ragged M=1999; N=5120): the columns that fill whole rounds equal,
     bit for bit, the unsplit variant's output, and the rest the split
     128x128 variant's, each run alone on the whole problem; nothing outside
     y or the workspace is written, and sampled rows meet the acceptance
     rule."""
-    M, N, K = 2048, 5120, 1024
+    N, K = 5120, 1024
     part_a, part_b, na = _hybrid_parts(name, M, N)
     assert 0 < na < N
     names = {fq.fp8q_gemm_config_name(i): i for i in range(fq.fp8q_gemm_num_configs())}

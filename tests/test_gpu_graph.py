@@ -161,19 +161,20 @@ def test_chain_graph_at_qwen3_8b_decode_shape():
         torch.cuda.synchronize()
 
 
-def test_stack_of_layers_in_one_graph_matches_eager():
+@pytest.mark.parametrize("mode", [fq.GROUP128, fq.PER_TOKEN], ids=["group128", "per-token"])
+def test_stack_of_layers_in_one_graph_matches_eager(mode):
     """Three layers with distinct weights and inputs recorded into one graph
     (capture_stack): every replay reproduces every layer's eager outputs,
     with eager work between the replays."""
     from fp8_block_scaled_rms_amd.graph import capture_stack
 
-    say("graph stack of 3 layers")
+    say("graph stack of 3 layers", mode)
     chains = []
     for layer in range(3):
-        chain, host_in = _build(f"stack{layer}", 8, 512, 768, 512, 2048, 1024, fq.GROUP128)
+        chain, host_in = _build(f"stack{layer}-{mode}", 8, 512, 768, 512, 2048, 1024, mode)
         chain.run()
         torch.cuda.synchronize()
-        _check_eager_against_oracle(chain, host_in, fq.GROUP128)
+        _check_eager_against_oracle(chain, host_in, mode)
         chains.append(chain)
     eager = [_snapshot(c) for c in chains]
     assert not _same(eager[0], eager[1])
