@@ -268,7 +268,14 @@ int fp8q_scaled_mm_blockwise_silu_quant(void* q, float* scale, const void* a, co
  * from the per-shape table; used by tests (every variant is checked) and by
  * the table's tuner.  cfg < 0 means "use the table".  Variant names start
  * with the engine: f16_ (exact: e4m3 widened losslessly to f16; every FP8
- * variant), i8_ (int8 op only).
+ * variant), i8_ (int8 op only).  Then the kind: _tiled_m<BM>_n<BN>_w<WM>x<WN>
+ * _st<stages> (LDS-staged tiles; _s<S>: K split over S workgroup rows, with
+ * fp32 partials in the workspace; _p: raised wave priority), _tiled_..._h<S>
+ * (hybrid: the column tiles that fill whole rounds of workgroups unsplit, the
+ * remaining columns on 128x128 tiles split S ways; its column split, and so
+ * its workspace size, depend on the current device's compute-unit count),
+ * _skinny_t<T>_r<R>_k<W>_j<J> (weight-streaming kernel for up to 16*T
+ * tokens).
  * Non-conforming opt-in: with the environment variable
  * FP8Q_NONCONFORMING_FP8_MFMA=1 set before the first GEMM call, the registry
  * also holds f8_ variants, which run the FP8 matrix instruction itself.  Its
